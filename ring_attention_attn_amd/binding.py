@@ -1,0 +1,194 @@
+"""ctypes binding of libringattn.so: the C ABI's calls under the same names.
+
+Argument marshalling only: tensors are passed as device pointers
+(``tensor.data_ptr()``) with the caller's current HIP stream; every computation
+runs in the library's kernels. A non-RA_OK status raises :class:`RaError`.
+Loading fails loudly if the library has not been built (``build()`` in
+``__graft_entry__`` or ``python -m ring_attention_attn_amd.build``); there is no
+fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
+
+RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EALIGN, RA_EDEVICE = 0, 1, 2, 3, 4
+RA_BF16, RA_F32 = 0, 1
+
+EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_bwd", "lse_merge", "ra_bwd_delta",
+           "head_permute", "ra_fill_f32", "ra_zigzag_positions", "ra_zigzag_segments",
+           "ra_double_ring_order", "ra_validate_step", "ra_status_str")
+
+
+class RaStepDesc(ctypes.Structure):
+    """Mirror of ``ra_step_desc`` in include/ring_attn.h (same field order)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("q_nseg", ctypes.c_int32), ("k_nseg", ctypes.c_int32),
+        ("q_seg_len", ctypes.c_int64), ("k_seg_len", ctypes.c_int64),
+        ("q_seg_pos", ctypes.c_int64 * 2), ("k_seg_pos", ctypes.c_int64 * 2),
+        ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q_ss", ctypes.c_int64), ("q_hs", ctypes.c_int64),
+        ("k_ss", ctypes.c_int64), ("k_hs", ctypes.c_int64),
+        ("v_ss", ctypes.c_int64), ("v_hs", ctypes.c_int64),
+        ("o_ss", ctypes.c_int64), ("o_hs", ctypes.c_int64),
+        ("do_ss", ctypes.c_int64), ("do_hs", ctypes.c_int64),
+        ("dk_ss", ctypes.c_int64), ("dk_hs", ctypes.c_int64),
+        ("dkv_accumulate", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class RaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loads on first use; raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python -m ring_attention_attn_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        pd = ctypes.POINTER(RaStepDesc)
+        sig = {
+            "ring_attn_step_fwd": [pd, vp, vp, vp, vp, vp, vp],
+            "ring_attn_step_bwd": [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "lse_merge": [i64, i32, i32, vp, vp, vp, vp, vp],
+            "ra_bwd_delta": [i64, i32, i32, i32, vp, vp, vp, vp, vp],
+            "head_permute": [vp, vp, i64, i32, i32, i32, i32, i32, vp],
+            "ra_fill_f32": [vp, i64, f32, vp],
+            "ra_zigzag_positions": [i64, i32, i32, vp],
+            "ra_zigzag_segments": [i64, i32, i32, vp, vp],
+            "ra_double_ring_order": [i32, i32, i32, vp],
+            "ra_validate_step": [pd, i32],
+            "ra_status_str": [i32],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "ra_status_str" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().ra_status_str(int(status)).decode()
+
+
+def _check(status, where):
+    if status != RA_OK:
+        raise RaError(status, where)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("tensors passed to libringattn must be contiguous "
+                         "(layouts are given by the descriptor's strides, not the tensor's)")
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- device calls
+
+def ring_attn_step_fwd(desc, q, k, v, o_step, lse_step, stream=None):
+    _check(lib().ring_attn_step_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o_step),
+                                    _ptr(lse_step), _stream(stream)), "ring_attn_step_fwd")
+
+
+def ring_attn_step_bwd(desc, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, stream=None):
+    _check(lib().ring_attn_step_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                    _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
+                                    _ptr(dv_acc), _stream(stream)), "ring_attn_step_bwd")
+
+
+def lse_merge(rows, hq, head_dim, o_acc, lse_acc, o_step, lse_step, stream=None):
+    _check(lib().lse_merge(rows, hq, head_dim, _ptr(o_acc), _ptr(lse_acc), _ptr(o_step),
+                           _ptr(lse_step), _stream(stream)), "lse_merge")
+
+
+def ra_bwd_delta(rows, hq, head_dim, dtype, o, dout, delta, o_out=None, stream=None):
+    _check(lib().ra_bwd_delta(rows, hq, head_dim, dtype, _ptr(o), _ptr(dout), _ptr(delta),
+                              _ptr(o_out), _stream(stream)), "ra_bwd_delta")
+
+
+def head_permute(src, dst, s, h, d, p, elem_bytes, inverse=0, stream=None):
+    _check(lib().head_permute(_ptr(src), _ptr(dst), s, h, d, p, elem_bytes, int(inverse),
+                              _stream(stream)), "head_permute")
+
+
+def ra_fill_f32(dst, n, value, stream=None):
+    _check(lib().ra_fill_f32(_ptr(dst), n, float(value), _stream(stream)), "ra_fill_f32")
+
+
+# ---------------------------------------------------------------- host helpers
+
+def ra_zigzag_positions(S, P, rank):
+    b = S // (2 * P) if P > 0 else 0
+    out = np.zeros(max(2 * b, 1), dtype=np.int64)
+    _check(lib().ra_zigzag_positions(S, P, rank, out.ctypes.data), "ra_zigzag_positions")
+    return out[:2 * b]
+
+
+def ra_zigzag_segments(S, P, rank):
+    pos = np.zeros(2, dtype=np.int64)
+    ln = np.zeros(1, dtype=np.int64)
+    _check(lib().ra_zigzag_segments(S, P, rank, pos.ctypes.data, ln.ctypes.data),
+           "ra_zigzag_segments")
+    return (int(pos[0]), int(pos[1])), int(ln[0])
+
+
+def ra_double_ring_order(inner, outer, rank):
+    out = np.zeros(max(inner * outer, 1), dtype=np.int32)
+    _check(lib().ra_double_ring_order(inner, outer, rank, out.ctypes.data), "ra_double_ring_order")
+    return out[:inner * outer]
+
+
+def ra_validate_step(desc, for_bwd=0):
+    return lib().ra_validate_step(ctypes.byref(desc), int(for_bwd))
+
+
+def make_desc(*, dtype, head_dim, hq, hkv, q_segments, k_segments, scale, causal=1,
+              q_strides, k_strides, v_strides, o_strides, do_strides=(0, 0), dk_strides=(0, 0),
+              dkv_accumulate=0):
+    """Fill a :class:`RaStepDesc`. ``*_segments`` = ((pos0[, pos1]), seg_len);
+    ``*_strides`` = (seq stride, head stride) in elements."""
+    d = RaStepDesc()
+    d.dtype, d.head_dim, d.hq, d.hkv = dtype, head_dim, hq, hkv
+    (qp, ql), (kp, kl) = q_segments, k_segments
+    d.q_nseg, d.k_nseg = len(qp), len(kp)
+    d.q_seg_len, d.k_seg_len = ql, kl
+    for i, x in enumerate(qp):
+        d.q_seg_pos[i] = x
+    for i, x in enumerate(kp):
+        d.k_seg_pos[i] = x
+    d.causal, d.scale = causal, scale
+    d.q_ss, d.q_hs = q_strides
+    d.k_ss, d.k_hs = k_strides
+    d.v_ss, d.v_hs = v_strides
+    d.o_ss, d.o_hs = o_strides
+    d.do_ss, d.do_hs = do_strides
+    d.dk_ss, d.dk_hs = dk_strides
+    d.dkv_accumulate = dkv_accumulate
+    return d

@@ -1,0 +1,186 @@
+// Bandwidth-bound kernels of the path: the log-sum-exp merge of step partials,
+// the backward preprocess D = rowsum(dO * O) (+ bf16 cast of O), the local head
+// permute of the head-parallel all-to-all, and a fill. All are HBM-bound: each
+// lane moves 16-byte vectors along the contiguous head_dim axis.
+#include <math.h>
+
+#include "ra_internal.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+
+inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 1 << 20) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+// ---------------------------------------------------------------- lse_merge
+// One thread per 4 consecutive floats of O; the D/4 threads of one (row, head)
+// vector sit in one wave, so every lane reads the old lse_acc before the one
+// lane that owns it stores the new value (in-order issue within a wave).
+template <int D>
+__global__ __launch_bounds__(kBlock) void lse_merge_kernel(int64_t rows, int32_t hq,
+                                                           float* __restrict__ o_acc,
+                                                           float* __restrict__ lse_acc,
+                                                           const float* __restrict__ o_step,
+                                                           const float* __restrict__ lse_step) {
+  constexpr int TPV = D / 4;  // threads per (row, head) vector
+  const int64_t nvec4 = rows * hq * TPV;
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < nvec4;
+       t += (int64_t)gridDim.x * kBlock) {
+    const int64_t vec = t / TPV;  // (row, head) pair, row-major
+    const int x4 = (int)(t % TPV);
+    const int64_t row = vec / hq;
+    const int h = (int)(vec % hq);
+    const int64_t li = (int64_t)h * rows + row;
+    const float la = lse_acc[li];
+    const float ls = lse_step[li];
+    const float m = fmaxf(la, ls);
+    if (m == -INFINITY) continue;  // both empty: leave the accumulator as it is
+    const float ea = expf(la - m), es = expf(ls - m);
+    const float tot = ea + es;
+    const float inv = 1.0f / tot;
+    const float ca = ea * inv, cs = es * inv;
+    f32x4* oa = reinterpret_cast<f32x4*>(o_acc + vec * D) + x4;
+    const f32x4 os = reinterpret_cast<const f32x4*>(o_step + vec * D)[x4];
+    f32x4 a = *oa;
+    a = ca * a + cs * os;
+    *oa = a;
+    if (x4 == 0) lse_acc[li] = m + logf(tot);
+  }
+}
+
+// ---------------------------------------------------------------- bwd delta
+// G = D/8 lanes per (row, head) vector, 8 elements per lane, reduced by xor
+// shuffles inside the lane group.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBlock) void bwd_delta_kernel(int64_t rows, int32_t hq,
+                                                           const float* __restrict__ o,
+                                                           const void* __restrict__ dout,
+                                                           float* __restrict__ delta,
+                                                           bf16_t* __restrict__ o_out) {
+  constexpr int G = D / 8;
+  const int64_t nvec = rows * hq;
+  const int64_t total = nvec * G;
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t - (threadIdx.x % G) < total;
+       t += (int64_t)gridDim.x * kBlock) {
+    const bool valid = t < total;
+    const int64_t vec = valid ? t / G : 0;
+    const int sub = (int)(t % G);
+    float acc = 0.f;
+    if (valid) {
+      const f32x4* op = reinterpret_cast<const f32x4*>(o + vec * D + sub * 8);
+      const f32x4 o0 = op[0], o1 = op[1];
+      float dv[8];
+      if (BF16) {
+        const bf16x8 g8 = *reinterpret_cast<const bf16x8*>((const bf16_t*)dout + vec * D + sub * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dv[e] = (float)g8[e];
+      } else {
+        const f32x4* gp = reinterpret_cast<const f32x4*>((const float*)dout + vec * D + sub * 8);
+        const f32x4 g0 = gp[0], g1 = gp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { dv[e] = g0[e]; dv[4 + e] = g1[e]; }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += dv[e] * o0[e] + dv[4 + e] * o1[e];
+      if (o_out) {
+        bf16x8 ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { ob[e] = (bf16_t)o0[e]; ob[4 + e] = (bf16_t)o1[e]; }
+        *reinterpret_cast<bf16x8*>(o_out + vec * D + sub * 8) = ob;
+      }
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, G);
+    if (valid && sub == 0) {
+      const int64_t row = vec / hq;
+      const int h = (int)(vec % hq);
+      delta[(int64_t)h * rows + row] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- head permute
+// A copy of s*p contiguous runs of R bytes: run (q, t) of the [p][s][h/p][d]
+// side is run (t, q) of the [s][h][d] side. 16-byte vectors, grid-stride.
+__global__ __launch_bounds__(kBlock) void head_permute_kernel(const uint4* __restrict__ src,
+                                                              uint4* __restrict__ dst, int64_t s,
+                                                              int32_t p, int64_t run16,
+                                                              int32_t inverse) {
+  const int64_t total = s * p * run16;
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * kBlock) {
+    // t indexes the [p][s] side (grouped) when writing forward, reading inverse
+    const int64_t run = t / run16, off = t % run16;
+    const int64_t q = run / s, tok = run % s;
+    const int64_t flat = (tok * p + q) * run16 + off;  // same vector on the [s][h] side
+    if (!inverse)
+      dst[t] = src[flat];
+    else
+      dst[flat] = src[t];
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_kernel(float* __restrict__ dst, int64_t n, float v) {
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * kBlock)
+    dst[t] = v;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, float* o_acc, float* lse_acc,
+                            const float* o_step, const float* lse_step, hipStream_t s) {
+  const int64_t work = rows * hq * (d / 4);
+  const unsigned g = grid_for(work, kBlock * 4, 8192);
+  if (d == 128)
+    hipLaunchKernelGGL(lse_merge_kernel<128>, dim3(g), dim3(kBlock), 0, s, rows, hq, o_acc,
+                       lse_acc, o_step, lse_step);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<64>, dim3(g), dim3(kBlock), 0, s, rows, hq, o_acc,
+                       lse_acc, o_step, lse_step);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(int64_t rows, int32_t hq, int32_t d, int32_t dtype, const float* o,
+                            const void* dout, float* delta, void* o_out, hipStream_t s) {
+  const int64_t work = rows * hq * (d / 8);
+  const unsigned g = grid_for(work, kBlock * 2, 8192);
+  bf16_t* ob = (bf16_t*)o_out;
+  if (d == 128) {
+    if (dtype == RA_BF16)
+      hipLaunchKernelGGL((bwd_delta_kernel<128, true>), dim3(g), dim3(kBlock), 0, s, rows, hq, o,
+                         dout, delta, ob);
+    else
+      hipLaunchKernelGGL((bwd_delta_kernel<128, false>), dim3(g), dim3(kBlock), 0, s, rows, hq, o,
+                         dout, delta, ob);
+  } else {
+    if (dtype == RA_BF16)
+      hipLaunchKernelGGL((bwd_delta_kernel<64, true>), dim3(g), dim3(kBlock), 0, s, rows, hq, o,
+                         dout, delta, ob);
+    else
+      hipLaunchKernelGGL((bwd_delta_kernel<64, false>), dim3(g), dim3(kBlock), 0, s, rows, hq, o,
+                         dout, delta, ob);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_head_permute(const void* src, void* dst, int64_t s, int32_t h, int32_t d,
+                               int32_t p, int32_t elem_bytes, int32_t inverse, hipStream_t st) {
+  const int64_t run16 = (int64_t)(h / p) * d * elem_bytes / 16;
+  const int64_t total = s * p * run16;
+  const unsigned g = grid_for(total, kBlock * 8, 16384);
+  hipLaunchKernelGGL(head_permute_kernel, dim3(g), dim3(kBlock), 0, st, (const uint4*)src,
+                     (uint4*)dst, s, p, run16, inverse);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* dst, int64_t n, float value, hipStream_t s) {
+  const unsigned g = grid_for(n, kBlock * 16, 16384);
+  hipLaunchKernelGGL(fill_kernel, dim3(g), dim3(kBlock), 0, s, dst, n, value);
+  return hipGetLastError();
+}

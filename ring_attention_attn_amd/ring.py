@@ -1,0 +1,85 @@
+"""Virtual ring over one GPU's share: the step sequence of ring attention with
+every step run by the library's kernels.
+
+On one device the ring is a loop over the KV chunks (all resident in HBM) in
+the double-ring visit order, where a multi-GPU ring would receive chunk j from
+its predecessor at step t ("Guide to LoongTrain", "The Communication Overhead
+and Causal Imbalance of Ring Attention"; "3. Double-Ring Asynchronous
+Communication Pipeline"). Forward: for each step, ring_attn_step_fwd then
+lse_merge into the running (O, LSE) -- the first step writes the running
+result directly. Backward: ra_bwd_delta (D = rowsum(dO O) and O in bf16), dq
+cleared with ra_fill_f32, then ring_attn_step_bwd per step with the final LSE.
+
+PyTorch only allocates device memory and provides the stream.
+"""
+import torch
+
+from . import binding as B
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+_RA_DTYPE = {"bf16": B.RA_BF16, "f32": B.RA_F32}
+
+
+class ShareRing:
+    """Buffers and precomputed step descriptors of one rank's share.
+
+    Inputs (caller-owned, contiguous): q [L][hq][d], K/V [P][L][hkv][d] (chunk j
+    = rows of blocks j and 2P-1-j), dout [L][hq][d]; L = 2b rows, b = S/(2P).
+    """
+
+    def __init__(self, S, inner, outer, rank, hq, hkv, d, dtype="bf16", scale=None,
+                 device="cuda", causal=1):
+        self.S, self.inner, self.outer, self.rank = S, inner, outer, rank
+        self.P = inner * outer
+        self.hq, self.hkv, self.d, self.dtype = hq, hkv, d, dtype
+        self.scale = scale if scale is not None else d ** -0.5
+        q_seg, b = B.ra_zigzag_segments(S, self.P, rank)
+        self.L = 2 * b
+        self.order = [int(j) for j in B.ra_double_ring_order(inner, outer, rank)]
+        f32 = dict(dtype=torch.float32, device=device)
+        L = self.L
+        self.o_acc = torch.empty((L, hq, d), **f32)
+        self.lse_acc = torch.empty((hq, L), **f32)
+        self.o_step = torch.empty((L, hq, d), **f32)
+        self.lse_step = torch.empty((hq, L), **f32)
+        self.delta = torch.empty((hq, L), **f32)
+        self.dq = torch.empty((L, hq, d), **f32)
+        self.dk = torch.empty((self.P, L, hkv, d), **f32)
+        self.dv = torch.empty((self.P, L, hkv, d), **f32)
+        self.o_lowp = torch.empty((L, hq, d), dtype=torch.bfloat16, device=device)
+        self.descs = []
+        for j in self.order:
+            k_seg, kb = B.ra_zigzag_segments(S, self.P, j)
+            desc = B.make_desc(dtype=_RA_DTYPE[dtype], head_dim=d, hq=hq, hkv=hkv,
+                               q_segments=(q_seg, b), k_segments=(k_seg, kb), scale=self.scale,
+                               causal=causal, q_strides=(hq * d, d), k_strides=(hkv * d, d),
+                               v_strides=(hkv * d, d), o_strides=(hq * d, d),
+                               do_strides=(hq * d, d), dk_strides=(hkv * d, d), dkv_accumulate=0)
+            self.descs.append((j, desc))
+
+    def forward(self, q, K, V, stream=None):
+        """Running (O fp32 [L][hq][d], LSE fp32 [hq][L]) after all P steps."""
+        for t, (j, desc) in enumerate(self.descs):
+            if t == 0:
+                B.ring_attn_step_fwd(desc, q, K[j], V[j], self.o_acc, self.lse_acc, stream)
+            else:
+                B.ring_attn_step_fwd(desc, q, K[j], V[j], self.o_step, self.lse_step, stream)
+                B.lse_merge(self.L, self.hq, self.d, self.o_acc, self.lse_acc, self.o_step,
+                            self.lse_step, stream)
+        return self.o_acc, self.lse_acc
+
+    def backward(self, q, K, V, dout, stream=None):
+        """dQ fp32 [L][hq][d] and per-chunk dK, dV fp32 [P][L][hkv][d] of this share,
+        using the forward's final O and LSE (call forward first)."""
+        B.ra_bwd_delta(self.L, self.hq, self.d, _RA_DTYPE[self.dtype], self.o_acc, dout,
+                       self.delta, self.o_lowp if self.dtype == "bf16" else None, stream)
+        B.ra_fill_f32(self.dq, self.dq.numel(), 0.0, stream)
+        for j, desc in self.descs:
+            B.ring_attn_step_bwd(desc, q, K[j], V[j], dout, self.lse_acc, self.delta, self.dq,
+                                 self.dk[j], self.dv[j], stream)
+        return self.dq, self.dk, self.dv
+
+    def step(self, q, K, V, dout, stream=None):
+        """One pass of the whole path: forward over all steps, then backward."""
+        self.forward(q, K, V, stream)
+        return self.backward(q, K, V, dout, stream)

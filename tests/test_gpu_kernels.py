@@ -1,0 +1,222 @@
+"""Kernel-level parity on the GPU: each C-ABI call against the fp64 oracle on
+the same seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from ring_attention_attn_amd import synth
+from tests.helpers import share_inputs, widen, to_device, assert_close, max_abs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ring_attention_attn_amd import binding
+    binding.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def B():
+    from ring_attention_attn_amd import binding
+    return binding
+
+
+# ------------------------------------------------------------------ head permute
+
+@pytest.mark.parametrize("s,h,d,p,eb", [(37, 8, 128, 4, 2), (64, 32, 128, 4, 2), (5, 6, 16, 3, 4),
+                                        (100, 8, 64, 8, 2), (16, 4, 128, 1, 2)])
+def test_head_permute_bit_exact(s, h, d, p, eb):
+    rng = np.random.default_rng(s + h)
+    dt = np.uint16 if eb == 2 else np.uint32
+    x = rng.integers(0, np.iinfo(dt).max, size=(s, h, d), dtype=dt)
+    tdt = torch.int16 if eb == 2 else torch.int32
+    src = torch.from_numpy(x.view(np.int16 if eb == 2 else np.int32)).cuda()
+    dst = torch.empty((p, s, h // p, d), dtype=tdt, device="cuda")
+    B().head_permute(src, dst, s, h, d, p, eb, 0)
+    back = torch.empty_like(src)
+    B().head_permute(dst, back, s, h, d, p, eb, 1)
+    torch.cuda.synchronize()
+    want = oracle.head_permute(x, p)
+    assert np.array_equal(dst.cpu().numpy().view(dt), want)
+    assert np.array_equal(back.cpu().numpy().view(dt), x)
+
+
+def test_head_permute_full_size_2d_attention_share():
+    """The 2D-Attention share's permute: 65,536 tokens x 32 heads x 128 bf16 into
+    4 head groups (and back), bit-exact."""
+    s, h, d, p = 65536, 32, 128, 4
+    x = synth.blocks_tensor(1003, synth.T_QPRE, [0], s, h, d, "bf16")
+    src = torch.from_numpy(x.view(np.int16)).cuda()
+    dst = torch.empty((p, s, h // p, d), dtype=torch.int16, device="cuda")
+    B().head_permute(src, dst, s, h, d, p, 2, 0)
+    back = torch.empty_like(src)
+    B().head_permute(dst, back, s, h, d, p, 2, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().view(np.uint16), oracle.head_permute(x, p))
+    assert torch.equal(back, src)
+
+
+# ------------------------------------------------------------------ merge / delta / fill
+
+@pytest.mark.parametrize("rows,hq,d", [(37, 3, 128), (256, 8, 64), (1, 1, 128)])
+def test_lse_merge(rows, hq, d):
+    rng = np.random.default_rng(rows)
+    oa = rng.standard_normal((rows, hq, d)).astype(np.float32)
+    os_ = rng.standard_normal((rows, hq, d)).astype(np.float32)
+    la = (rng.standard_normal((hq, rows)) * 3).astype(np.float32)
+    ls = (rng.standard_normal((hq, rows)) * 3).astype(np.float32)
+    # empty rows: one side, the other side, both
+    la[:, ::5] = -np.inf
+    ls[:, ::7] = -np.inf
+    oa[::5] = 0.0
+    os_[::7] = 0.0
+    want_o, want_l = oracle.lse_merge(oa, la, os_, ls)
+    t = [torch.from_numpy(a.copy()).cuda() for a in (oa, la, os_, ls)]
+    B().lse_merge(rows, hq, d, t[0], t[1], t[2], t[3])
+    torch.cuda.synchronize()
+    got_o, got_l = t[0].cpu().numpy(), t[1].cpu().numpy()
+    assert not np.isnan(got_o).any() and not np.isnan(got_l).any()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(want_l))
+    assert max_abs(got_o, want_o) < 2e-6
+    assert max_abs(got_l, want_l) < 2e-6
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_bwd_delta_and_cast(dtype, d):
+    rows, hq = 301, 5
+    rng = np.random.default_rng(d)
+    o = rng.standard_normal((rows, hq, d)).astype(np.float32)
+    g = synth.blocks_tensor(9, synth.T_DO, [0], rows, hq, d, dtype)
+    want = np.einsum("lhd,lhd->hl", widen(g, dtype), o.astype(np.float64))
+    to = torch.from_numpy(o).cuda()
+    tg = to_device(g, dtype)
+    delta = torch.empty((hq, rows), dtype=torch.float32, device="cuda")
+    ob = torch.empty((rows, hq, d), dtype=torch.bfloat16, device="cuda")
+    B().ra_bwd_delta(rows, hq, d, B().RA_BF16 if dtype == "bf16" else B().RA_F32, to, tg, delta, ob)
+    torch.cuda.synchronize()
+    assert max_abs(delta.cpu().numpy(), want) < 1e-4
+    ref_bits = synth.f32_to_bf16_bits(o)
+    assert np.array_equal(ob.cpu().view(torch.int16).numpy().view(np.uint16), ref_bits)
+
+
+def test_fill():
+    x = torch.empty(1000003, dtype=torch.float32, device="cuda")
+    B().ra_fill_f32(x, x.numel(), -2.5)
+    torch.cuda.synchronize()
+    assert bool((x == -2.5).all())
+
+
+# ------------------------------------------------------------------ step forward / backward
+
+STEP_CASES = [
+    # dtype, d, hq, hkv, b, P, r, causal
+    ("bf16", 128, 8, 2, 200, 4, 1, 1),    # GQA 4, ragged rows (400 local rows)
+    ("bf16", 64, 4, 4, 96, 3, 2, 1),      # MHA, d=64
+    ("bf16", 128, 8, 1, 256, 2, 0, 1),    # GQA 8
+    ("bf16", 128, 4, 2, 130, 2, 1, 1),    # GQA 2, tiles crossing the segment boundary
+    ("bf16", 128, 4, 1, 72, 2, 0, 0),     # non-causal
+    ("f32", 64, 1, 1, 64, 4, 3, 1),       # the fp32 workload's shape
+    ("f32", 128, 4, 2, 40, 2, 1, 1),
+]
+
+
+def _desc(dtype, d, hq, hkv, S, P, r, j, causal, dkv_acc=0):
+    (qp, b) = B().ra_zigzag_segments(S, P, r)
+    (kp, _) = B().ra_zigzag_segments(S, P, j)
+    return B().make_desc(dtype=B().RA_BF16 if dtype == "bf16" else B().RA_F32, head_dim=d, hq=hq,
+                         hkv=hkv, q_segments=(qp, b), k_segments=(kp, b), scale=1 / math.sqrt(d),
+                         causal=causal, q_strides=(hq * d, d), k_strides=(hkv * d, d),
+                         v_strides=(hkv * d, d), o_strides=(hq * d, d), do_strides=(hq * d, d),
+                         dk_strides=(hkv * d, d), dkv_accumulate=dkv_acc)
+
+
+def _oracle_step_fwd(x, S, P, r, j, d, dtype, causal):
+    pos_q = oracle.zigzag_positions(S, P, r)
+    pos_k = oracle.zigzag_positions(S, P, j)
+    if not causal:
+        pos_q = np.full_like(pos_q, S)   # every key visible
+    return oracle.step_forward(widen(x["q"], dtype), widen(x["k_ch"][j], dtype),
+                               widen(x["v_ch"][j], dtype), pos_q, pos_k, 1 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_step_forward(case):
+    dtype, d, hq, hkv, b, P, r, causal = case
+    S = 2 * P * b
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=77)
+    L = 2 * b
+    q = to_device(x["q"], dtype)
+    kc = to_device(x["k_ch"], dtype)
+    vc = to_device(x["v_ch"], dtype)
+    for j in range(P):
+        o = torch.full((L, hq, d), float("nan"), device="cuda")
+        lse = torch.full((hq, L), float("nan"), device="cuda")
+        B().ring_attn_step_fwd(_desc(dtype, d, hq, hkv, S, P, r, j, causal), q, kc[j], vc[j], o, lse)
+        torch.cuda.synchronize()
+        want_o, want_l = _oracle_step_fwd(x, S, P, r, j, d, dtype, causal)
+        got_l = lse.cpu().numpy()
+        assert np.array_equal(np.isneginf(got_l), np.isneginf(want_l)), f"chunk {j}: empty rows"
+        assert_close(f"O chunk {j}", o.cpu().numpy(), want_o, dtype)
+        assert_close(f"LSE chunk {j}", got_l, want_l, dtype, is_lse=True)
+
+
+def test_step_forward_empty_chunk():
+    d, hq, hkv, S, P, r = 128, 4, 2, 512, 2, 0
+    desc = _desc("bf16", d, hq, hkv, S, P, r, 1, 1)
+    desc.k_seg_len = 0
+    L = S // P
+    q = torch.zeros((L, hq, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((L, hq, d), float("nan"), device="cuda")
+    lse = torch.zeros((hq, L), device="cuda")
+    B().ring_attn_step_fwd(desc, q, 0, 0, o, lse)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_step_backward(case):
+    dtype, d, hq, hkv, b, P, r, causal = case
+    S = 2 * P * b
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=78)
+    L = 2 * b
+    scale = 1 / math.sqrt(d)
+    pos_q = oracle.zigzag_positions(S, P, r)
+    if not causal:
+        pos_q = np.full_like(pos_q, S)
+    q64, do64 = widen(x["q"], dtype), widen(x["do"], dtype)
+    full = oracle.share_backward(q64, widen(x["k_nat"], dtype), widen(x["v_nat"], dtype), do64,
+                                 pos_q, scale)
+    q = to_device(x["q"], dtype)
+    do = to_device(x["do"], dtype)
+    kc = to_device(x["k_ch"], dtype)
+    vc = to_device(x["v_ch"], dtype)
+    lse = torch.from_numpy(np.ascontiguousarray(full["LSE"], dtype=np.float32)).cuda()
+    delta = torch.from_numpy(np.ascontiguousarray(full["D"], dtype=np.float32)).cuda()
+    for j in range(P):
+        pos_k = oracle.zigzag_positions(S, P, j)
+        want_dq, want_dk, want_dv = oracle.step_backward(
+            q64, widen(x["k_ch"][j], dtype), widen(x["v_ch"][j], dtype), do64, full["LSE"],
+            full["D"], pos_q, pos_k, scale)
+        dq = torch.zeros((L, hq, d), device="cuda")
+        dk = torch.full((L, hkv, d), float("nan"), device="cuda")
+        dv = torch.full((L, hkv, d), float("nan"), device="cuda")
+        B().ring_attn_step_bwd(_desc(dtype, d, hq, hkv, S, P, r, j, causal), q, kc[j], vc[j], do,
+                               lse, delta, dq, dk, dv)
+        torch.cuda.synchronize()
+        assert_close(f"dQ chunk {j}", dq.cpu().numpy(), want_dq, dtype)
+        assert_close(f"dK chunk {j}", dk.cpu().numpy(), want_dk, dtype)
+        assert_close(f"dV chunk {j}", dv.cpu().numpy(), want_dv, dtype)
+        # accumulate mode adds to what is there
+        B().ring_attn_step_bwd(_desc(dtype, d, hq, hkv, S, P, r, j, causal, dkv_acc=1), q, kc[j],
+                               vc[j], do, lse, delta, dq, dk, dv)
+        torch.cuda.synchronize()
+        assert_close(f"2 dK chunk {j}", dk.cpu().numpy(), 2 * want_dk, dtype)
+        assert_close(f"2 dV chunk {j}", dv.cpu().numpy(), 2 * want_dv, dtype)

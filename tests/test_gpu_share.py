@@ -1,0 +1,152 @@
+"""Whole-share parity on the GPU: the virtual ring (P forward steps + merges,
+backward preprocess, P backward steps) against the fp64 oracle of full-sequence
+causal attention restricted to the share's rows.
+
+Small shares are compared element by element; the full-size workload that the
+benchmark times is compared on sampled rows and keys that the oracle computes
+one by one, plus identities that hold at any size."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from ring_attention_attn_amd.configs import CONFIGS
+from tests.helpers import share_inputs, widen, to_device, assert_close, max_abs, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ring_attention_attn_amd import binding
+    binding.lib()
+    yield
+
+
+def run_share(S, inner, outer, r, hq, hkv, d, dtype, x):
+    from ring_attention_attn_amd.ring import ShareRing
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype)
+    q, do = to_device(x["q"], dtype), to_device(x["do"], dtype)
+    K, V = to_device(x["k_ch"], dtype), to_device(x["v_ch"], dtype)
+    o, lse = ring.forward(q, K, V)
+    dq, dk, dv = ring.backward(q, K, V, do)
+    torch.cuda.synchronize()
+    return ring, dict(O=o.cpu().numpy(), LSE=lse.cpu().numpy(), dQ=dq.cpu().numpy(),
+                      dK=dk.cpu().numpy(), dV=dv.cpu().numpy(), Obf=ring.o_lowp)
+
+
+SHARE_CASES = [
+    # name, S, inner, outer, rank, hq, hkv, d, dtype
+    ("tiny_f32_r0", 512, 4, 1, 0, 1, 1, 64, "f32"),
+    ("tiny_f32_r1", 512, 4, 1, 1, 1, 1, 64, "f32"),
+    ("tiny_f32_r2", 512, 4, 1, 2, 1, 1, 64, "f32"),
+    ("tiny_f32_r3", 512, 4, 1, 3, 1, 1, 64, "f32"),
+    ("gqa4_ring4_r0", 8192, 4, 1, 0, 8, 2, 128, "bf16"),
+    ("gqa4_ring4_r3", 8192, 4, 1, 3, 8, 2, 128, "bf16"),
+    ("gqa8_double_ring_4x2_r5", 4096, 4, 2, 5, 8, 1, 128, "bf16"),
+    ("mha_ring8_ragged_r6", 8 * 2 * 88, 8, 1, 6, 4, 4, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SHARE_CASES, ids=lambda c: c[0])
+def test_share_matches_oracle(case):
+    name, S, inner, outer, r, hq, hkv, d, dtype = case
+    P = inner * outer
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=1000 + S + r)
+    _, got = run_share(S, inner, outer, r, hq, hkv, d, dtype, x)
+    pos = oracle.zigzag_positions(S, P, r)
+    want = oracle.share_backward(widen(x["q"], dtype), widen(x["k_nat"], dtype),
+                                 widen(x["v_nat"], dtype), widen(x["do"], dtype), pos, 1 / math.sqrt(d))
+    assert_close("O", got["O"], want["O"], dtype)
+    assert_close("LSE", got["LSE"], want["LSE"], dtype, is_lse=True)
+    assert_close("dQ", got["dQ"], want["dQ"], dtype)
+    b = S // (2 * P)
+    for j in range(P):
+        kp = oracle.zigzag_positions(S, P, j)
+        assert_close(f"dK[{j}]", got["dK"][j], want["dK"][kp], dtype)
+        assert_close(f"dV[{j}]", got["dV"][j], want["dV"][kp], dtype)
+    if dtype == "bf16":
+        # per zigzag half, so that a wrong short-row block cannot hide in the average
+        for half in (slice(0, b), slice(b, 2 * b)):
+            assert rel_l2(got["O"][half], want["O"][half]) < 1e-2
+            assert rel_l2(got["dQ"][half], want["dQ"][half]) < 1e-2
+
+
+def test_ring_order_invariance():
+    """The merged result does not depend on the order the chunks are visited in
+    (up to fp32 rounding of the merge)."""
+    from ring_attention_attn_amd import binding as B
+    from ring_attention_attn_amd.ring import ShareRing
+    S, inner, outer, r, hq, hkv, d = 4096, 4, 2, 3, 8, 2, 128
+    x = share_inputs(S, inner * outer, r, hq, hkv, d, "bf16", seed=5)
+    q, do = to_device(x["q"], "bf16"), to_device(x["do"], "bf16")
+    K, V = to_device(x["k_ch"], "bf16"), to_device(x["v_ch"], "bf16")
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, "bf16")
+    o1 = ring.forward(q, K, V)[0].clone()
+    ring.descs = ring.descs[::-1]
+    o2 = ring.forward(q, K, V)[0].clone()
+    torch.cuda.synchronize()
+    assert max_abs(o1.cpu().numpy(), o2.cpu().numpy()) < 1e-5
+
+
+def _sample_rows(b, n_rand, seed):
+    fixed = [0, 1, 31, 32, 63, 64, 127, b - 1, b, b + 1, b + 63, 2 * b - 64, 2 * b - 1]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([fixed, rng.integers(0, 2 * b, n_rand)]))
+
+
+@pytest.mark.parametrize("cfg_name", ["llama3_8b_cp8_128k"])
+def test_full_size_share_sampled(cfg_name):
+    """The benchmark's workload at full size and in its launch configuration.
+
+    Sampled query rows (both zigzag halves, tile edges) of several heads: O, LSE
+    and dQ from the oracle row by row. Sampled late keys (the last 64 positions,
+    seen only by this rank's last rows): dK and dV from the oracle. Identities
+    over all keys: sum_k dV_k = sum of dO over the group's rows and heads, and
+    sum_k dK_k = 0."""
+    cfg = CONFIGS[cfg_name]
+    S, P, r, hq, hkv, d = cfg.S, cfg.P, 0, cfg.hq, cfg.hkv, cfg.d
+    G = hq // hkv
+    scale = 1 / math.sqrt(d)
+    x = share_inputs(S, P, r, hq, hkv, d, "bf16", seed=cfg.seed)
+    _, got = run_share(S, cfg.inner, cfg.outer, r, hq, hkv, d, "bf16", x)
+    b = S // (2 * P)
+    pos = oracle.zigzag_positions(S, P, r)
+    rows = _sample_rows(b, 24, cfg.seed)
+    for h in (0, G - 1, hq // 2 + 1, hq - 1):
+        g = h // G
+        kg = widen(x["k_nat"][:, g:g + 1], "bf16")
+        vg = widen(x["v_nat"][:, g:g + 1], "bf16")
+        qr = widen(x["q"][rows][:, h:h + 1], "bf16")
+        dor = widen(x["do"][rows][:, h:h + 1], "bf16")
+        res = oracle.share_backward(qr, kg, vg, dor, pos[rows], scale)
+        assert_close(f"O h{h}", got["O"][rows][:, h:h + 1], res["O"], "bf16")
+        assert_close(f"LSE h{h}", got["LSE"][h:h + 1, rows], res["LSE"], "bf16", is_lse=True)
+        assert_close(f"dQ h{h}", got["dQ"][rows][:, h:h + 1], res["dQ"], "bf16")
+    # late keys: positions S-64 .. S-1 = chunk 0's back block tail
+    key_pos = np.arange(S - 64, S)
+    key_rows = b + (key_pos - (2 * P - 1) * b)          # rows of chunk 0 (and of this rank)
+    for g in (0, hkv - 1):
+        heads = slice(g * G, (g + 1) * G)
+        kg = widen(x["k_nat"][:, g:g + 1], "bf16")
+        vg = widen(x["v_nat"][:, g:g + 1], "bf16")
+        qr = widen(x["q"][key_rows][:, heads], "bf16")
+        dor = widen(x["do"][key_rows][:, heads], "bf16")
+        fw = oracle.share_backward(qr, kg, vg, dor, pos[key_rows], scale)
+        _, dk, dv = oracle.step_backward(qr, kg[key_pos], vg[key_pos], dor, fw["LSE"], fw["D"],
+                                         pos[key_rows], key_pos, scale)
+        assert_close(f"dK late g{g}", got["dK"][0][key_rows][:, g:g + 1], dk, "bf16")
+        assert_close(f"dV late g{g}", got["dV"][0][key_rows][:, g:g + 1], dv, "bf16")
+    dk_all = got["dK"].astype(np.float64)
+    dv_all = got["dV"].astype(np.float64)
+    do64 = widen(x["do"], "bf16")
+    for g in range(hkv):
+        want_sum = do64[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        np.testing.assert_allclose(dv_all[:, :, g].sum(axis=(0, 1)), want_sum,
+                                   atol=1e-3 * np.abs(want_sum).max() + 1e-2)
+        s = dk_all[:, :, g].sum(axis=(0, 1))
+        assert np.abs(s).max() <= 1e-3 * np.abs(dk_all[:, :, g]).sum(axis=(0, 1)).max()
