@@ -75,7 +75,7 @@ typedef struct ra_step_desc {
   int64_t q_seg_len, k_seg_len;    /* >= 0; a zero-row call is a no-op             */
   int64_t q_seg_pos[2], k_seg_pos[2]; /* global position of each segment's row 0   */
   int32_t causal;       /* 1: key visible iff pos_k <= pos_q; 0: all keys visible  */
-  float scale;          /* softmax scale, normally 1/sqrt(head_dim)                */
+  float scale;          /* softmax scale > 0, normally 1/sqrt(head_dim)            */
   int64_t q_ss, q_hs;   /* q    [lq][hq][d]                                        */
   int64_t k_ss, k_hs;   /* k    [lk][hkv][d]                                       */
   int64_t v_ss, v_hs;   /* v    [lk][hkv][d]                                       */
@@ -112,8 +112,10 @@ ra_status ring_attn_step_fwd(const ra_step_desc* desc, const void* q, const void
  *   dq_acc[i][h]  += scale * sum_j dS_ij k_j          (always accumulates)
  *   dk_acc[j][g]  (+)= scale * sum_{h in g, i} dS_ij q_i
  *   dv_acc[j][g]  (+)= sum_{h in g, i} P_ij dout_i    (per desc->dkv_accumulate)
- * dq_acc must be initialised by the caller (e.g. ra_fill_f32 to 0). dq_acc is
- * updated with fp32 atomics, so its rounding order is not deterministic.
+ * dq_acc must be initialised by the caller (e.g. ra_fill_f32 to 0). Every
+ * element of dq_acc, dk_acc and dv_acc is read-modify-written by one thread,
+ * so results are deterministic; calls that overlap on the same accumulators
+ * race. bf16 runs two kernels (dQ; dK and dV) on `stream`, in that order.
  */
 ra_status ring_attn_step_bwd(const ra_step_desc* desc, const void* q, const void* k,
                              const void* v, const void* dout, const float* lse,

@@ -28,13 +28,13 @@ CFLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(src_dir=CSRC):
+    return sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir) if f.endswith(".hip"))
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+def _compile(src, verbose, build_dir, extra):
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC] + CFLAGS + list(extra) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -45,18 +45,20 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+def build(verbose=False, out=OUT, src_dir=CSRC, build_dir=BUILD, extra_flags=()):
+    """Compile every source in ``src_dir`` and link ``out``. ``extra_flags`` are
+    appended to each compile (e.g. -D tile settings)."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sources(src_dir)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra_flags), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -27,8 +27,10 @@ ra_status check_strides(int64_t ss, int64_t hs, int64_t rows, int32_t heads, int
 ra_status check_seg(int32_t nseg, int64_t seg_len, const int64_t* pos) {
   if (nseg != 1 && nseg != 2) return RA_EINVAL;
   if (seg_len < 0) return RA_EINVAL;
-  for (int i = 0; i < nseg; ++i)
+  for (int i = 0; i < nseg; ++i) {
     if (pos[i] < 0 || pos[i] > (INT64_MAX / 4)) return RA_EINVAL;
+    if (pos[i] + seg_len > (int64_t)INT32_MAX - 64) return RA_EUNSUPPORTED;  // kernels use int32
+  }
   return RA_OK;
 }
 
@@ -64,7 +66,7 @@ ra_status ra_validate_step(const ra_step_desc* d, int32_t for_bwd) {
   if (d->head_dim != 64 && d->head_dim != 128) return RA_EUNSUPPORTED;
   if (d->hq < 1 || d->hkv < 1 || d->hq % d->hkv != 0) return RA_EINVAL;
   if (d->causal != 0 && d->causal != 1) return RA_EINVAL;
-  if (!isfinite(d->scale)) return RA_EINVAL;
+  if (!isfinite(d->scale) || !(d->scale > 0.f)) return RA_EINVAL;
   if (d->dkv_accumulate != 0 && d->dkv_accumulate != 1) return RA_EINVAL;
   ra_status st;
   if ((st = check_seg(d->q_nseg, d->q_seg_len, d->q_seg_pos)) != RA_OK) return st;

@@ -3,20 +3,31 @@
 // dP = dO V^T, dS = P (dP - D): dV += P^T dO, dK += scale dS^T Q,
 // dQ += scale dS K; dK/dV sum over the query heads sharing a KV head.
 //
-// bf16 path (gfx950 MFMA), key-stationary: a workgroup of 4 waves owns 128 keys
-// of one KV head (32 per wave, K and V held in registers as MFMA operands) and
-// walks the query tiles (64 rows) of every query head of the group. Per tile a
-// wave computes S = Q K^T and dP = dO V^T (lanes = keys, registers = queries),
-// so P and dS are directly the B operands of dV^T += dO^T P and
-// dK^T += Q^T dS, with dO^T and Q^T read from LDS by ds_read_b64_tr_b16. dS is
-// also written to LDS (key-major), and the workgroup forms
-// dQ_tile = dS K over its 128 keys, added to dq_acc with fp32 atomics.
+// bf16 path (gfx950 MFMA): two deterministic kernels, one per output side
+// (described at each kernel): a query-stationary dQ kernel and a
+// key-stationary dK/dV kernel. The dQ kernel recomputes S and dP instead of
+// exchanging dS through memory, which trades two extra products for no
+// atomics and two waves per SIMD.
 //
 // fp32 path: plain VALU kernels, one per output (dQ row-stationary, dK/dV
 // key-stationary), deterministic.
+#include <limits.h>
 #include <math.h>
 
 #include "ra_internal.h"
+#include "ra_tile.h"
+
+// minimum resident workgroups per CU of the dQ kernel
+#ifndef RA_BWD_DQ_MINB
+#define RA_BWD_DQ_MINB 2
+#endif
+// 1: transposed operand tiles staged in LDS; 0: read with ds_read_b64_tr_b16
+#ifndef RA_BWD_KTT
+#define RA_BWD_KTT 0
+#endif
+#ifndef RA_BWD_QTT
+#define RA_BWD_QTT 0
+#endif
 
 namespace {
 
@@ -177,52 +188,214 @@ __global__ __launch_bounds__(64) void bwd_dkv_simple_kernel(StepParams p) {
   }
 }
 
-// ============================================================= MFMA kernel
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ inline bf16x4 ds_read_tr(const bf16_t* lds_ptr) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
-  return __builtin_bit_cast(bf16x4, r);
+// ============================================================= MFMA kernels
+// Operand A of a product that contracts over rows of a tile held row-major in
+// LDS (K for dQ^T += K^T dS^T; Q, dO for dK^T, dV^T): 8 values per lane from
+// rows base + 8*hi + 0..7 at column col0 + l32 -- either one 16-byte read of a
+// transposed copy (TRANSPOSED) or two transposing reads of the row-major tile.
+template <bool TRANSPOSED, int RSTR, int TSTR>
+__device__ __forceinline__ bf16x8 rows_operand(const bf16_t* rows_tile, const bf16_t* cols_tile,
+                                               int base, int col0, int lane) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  if (TRANSPOSED) return *(const bf16x8*)(cols_tile + (col0 + l32) * TSTR + base + 8 * hi);
+  const int grp = lane >> 4, gi = lane & 15;
+  const bf16_t* b = rows_tile + (base + 8 * hi + (gi >> 2)) * RSTR + col0 + 16 * (grp & 1) + 4 * (gi & 3);
+  const bf16x4 lo4 = ds_read_tr(b);
+  const bf16x4 hi4 = ds_read_tr(b + 4 * RSTR);
+  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// A 32x16 (or 16x32) MFMA operand slice whose 8 contraction values per lane
-// come from 4+4 consecutive LDS rows at one column: rows base_row + tr_row and
-// base_row + 8 + tr_row, column base_col + tr_col (lane roles precomputed).
-__device__ inline bf16x8 tr_operand(const bf16_t* lds, int stride, int row, int col) {
-  const bf16x4 a = ds_read_tr(lds + row * stride + col);
-  const bf16x4 b = ds_read_tr(lds + (row + 8) * stride + col);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(StepParams p, int n_kt) {
-  constexpr int KB = 128;         // keys per workgroup, 32 per wave
-  constexpr int QT = 64;          // query rows per iteration (two 32-row blocks)
+// (1) dQ, query-stationary: like the forward, a wave owns 32 query rows of one
+//     head and streams 64-key tiles. S^T = K Q^T and dP^T = V dO^T put a query
+//     in each lane, so LSE and D are per-lane scalars; dS^T (bf16, 8
+//     consecutive keys per register chunk thanks to the sigma row order) is the
+//     B operand of dQ^T += K^T dS^T. dq_acc is read-modify-written once per row
+//     at the end: no atomics.
+template <int D, bool KTT>
+__global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams p, int hpw,
+                                                                     int n_qt, int rows_per_wg) {
+  constexpr int KT = 64;
+  constexpr int KSTR = D + 16;
+  constexpr int KTSTR = KT + 8;
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  constexpr int NDW = ND / 2;     // dQ d-blocks per wave
-  constexpr int QSTR = D + 16;    // LDS strides (elements)
-  constexpr int KSTR = D + 16;
-  constexpr int SSTR = QT + 16;
-  constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int NLQ = QT * CPR / 256;
-  constexpr int NLK = KB * CPR / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[QT * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sdO[QT * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KB * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sdsT[KB * SSTR];
-  __shared__ float sL[QT], sDl[QT];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[KT * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[KTT ? D * KTSTR : 8];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int l32 = lane & 31, hi = lane >> 5;
-  const int grp = lane >> 4, gi = lane & 15;
-  const int tr_row = 4 * (grp >> 1) + (gi >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
+  const int srow = sigma32(l32);
 
-  const int total = p.hkv * n_kt;
-  const int w = blockIdx.x;
-  const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
+  const int nsub = p.group / hpw;
+  const int total = p.hkv * nsub * n_qt;
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int gh = logical / n_qt;
+  const int qt = n_qt - 1 - (logical % n_qt);
+  const int g = gh / nsub, hs = gh % nsub;
+  const int h = g * p.group + hs * hpw + (wave % hpw);
+  const int64_t lq = p.qm.len, lk = p.km.len;
+  const int64_t wg_r0 = (int64_t)qt * rows_per_wg;
+  const int64_t row0 = wg_r0 + (int64_t)(wave / hpw) * 32;
+
+  int64_t wq_lo = 0, wq_hi = -1, gq_lo, gq_hi;
+  const bool wave_active = row0 < lq;
+  if (wave_active) seg_bounds(p.qm, row0, row0 + 32 < lq ? row0 + 32 : lq, wq_lo, wq_hi);
+  seg_bounds(p.qm, wg_r0, wg_r0 + rows_per_wg < lq ? wg_r0 + rows_per_wg : lq, gq_lo, gq_hi);
+
+  const bf16_t* K = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
+  const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
+
+  const int64_t qrow = row0 + l32;
+  const bool qok = qrow < lq;
+  const int qpos = qok ? (int)seg_pos(p.qm, qrow) : -1;
+  const int qlim = (p.causal || !qok) ? qpos : INT_MAX;  // last visible key position
+  bf16x8 qreg[NC], doreg[NC];
+  {
+    const bf16_t* Q = (const bf16_t*)p.q + qrow * p.q_ss + (int64_t)h * p.q_hs + 8 * hi;
+    const bf16_t* G = (const bf16_t*)p.dout + qrow * p.do_ss + (int64_t)h * p.do_hs + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 z = {};
+      qreg[c] = qok ? *(const bf16x8*)(Q + 16 * c) : z;
+      doreg[c] = qok ? *(const bf16x8*)(G + 16 * c) : z;
+    }
+  }
+  float lse2 = INFINITY, dl = 0.f;  // invalid or empty rows: P = 0
+  if (qok) {
+    const float lse = p.lse_in[(int64_t)h * lq + qrow];
+    lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    dl = p.delta[(int64_t)h * lq + qrow];
+  }
+
+  f32x16 qacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) qacc[db] = f32x16{};
+
+  const int n_kt = (int)((lk + KT - 1) / KT);
+  auto tile_bounds = [&](int t, int64_t& lo, int64_t& hi_) {
+    const int64_t k0 = (int64_t)t * KT;
+    seg_bounds(p.km, k0, k0 + KT < lk ? k0 + KT : lk, lo, hi_);
+  };
+  auto next_visible = [&](int t) {
+    while (t < n_kt) {
+      if (!p.causal) return t;
+      int64_t lo, hh;
+      tile_bounds(t, lo, hh);
+      if (lo <= gq_hi) return t;
+      ++t;
+    }
+    return t;
+  };
+
+  RowStage<KT, D, KSTR> ks, vs;
+  ColStage<KT, D, KTSTR> kts;
+  ks.init(p.k_ss, tid);
+  vs.init(p.v_ss, tid);
+  if (KTT) kts.init(p.k_ss, tid);
+  auto load_tile = [&](int t) {
+    ks.load(K, p.k_ss, (int64_t)t * KT, lk);
+    vs.load(V, p.v_ss, (int64_t)t * KT, lk);
+    if (KTT) kts.load(K, p.k_ss, (int64_t)t * KT, lk);
+  };
+  int t = next_visible(0);
+  if (t < n_kt) load_tile(t);
+  while (t < n_kt) {
+    __syncthreads();
+    ks.store(sK);
+    vs.store(sV);
+    if (KTT) kts.store(sKt);
+    __syncthreads();
+    const int tn = next_visible(t + 1);
+    if (tn < n_kt) load_tile(tn);
+    int64_t klo, khi;
+    tile_bounds(t, klo, khi);
+    const bool wave_skip = !wave_active || (p.causal && klo > wq_hi);
+    if (!wave_skip) {
+      const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
+      const TilePos tp(p.km, (int64_t)t * KT, KT);
+      bf16x8 dsk[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int off = (kb * 32 + srow) * KSTR + 16 * c + 8 * hi;
+          sacc = mfma32(*(const bf16x8*)(sK + off), qreg[c], sacc);
+          pacc = mfma32(*(const bf16x8*)(sV + off), doreg[c], pacc);
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          bf16x8 v8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
+            if (need_mask) {
+              const int off = kb * 32 + 16 * hf + 8 * hi + e;
+              const bool vis = (off < tp.nvalid) & (tp.pos(off) <= qlim);
+              pr = vis ? pr : 0.f;
+            }
+            v8[e] = (bf16_t)(pr * (pacc[r] - dl));
+          }
+          dsk[kb][hf] = v8;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const bf16x8 a = rows_operand<KTT, KSTR, KTSTR>(sK, sKt, 16 * cc, 32 * db, lane);
+          qacc[db] = mfma32(a, dsk[cc >> 1][cc & 1], qacc[db]);
+        }
+      }
+    }
+    t = tn;
+  }
+  if (!qok) return;
+  float* dq = p.o + qrow * p.o_ss + (int64_t)h * p.o_hs;
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4* ptr = (f32x4*)(dq + 32 * db + 8 * i + 4 * hi);
+      f32x4 v4 = *ptr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] += qacc[db][4 * i + j] * p.scale;
+      *ptr = v4;
+    }
+}
+
+// (2) dK, dV, key-stationary: a workgroup of 4 waves owns 128 keys of one KV
+//     head (32 per wave; K^T and V^T B operands held in registers) and walks the
+//     64-row query tiles of every query head of the group. S = Q K^T and
+//     dP = dO V^T put a key in each lane (query rows fed in sigma order), so P
+//     and dS, rounded to bf16, are directly the B operands of dV^T += dO^T P and
+//     dK^T += Q^T dS. Each dK/dV element has one writer.
+template <int D, bool QTT>
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
+  constexpr int KB = 128;
+  constexpr int QT = 64;
+  constexpr int QSTR = D + 16;
+  constexpr int QTSTR = QT + 8;
+  constexpr int NC = D / 16;
+  constexpr int ND = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[QT * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t sdO[QT * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[QTT ? D * QTSTR : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t sdOt[QTT ? D * QTSTR : 8];
+  __shared__ __attribute__((aligned(16))) float sL[QT];
+  __shared__ __attribute__((aligned(16))) float sDl[QT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int srow = sigma32(l32);
+
+  const int logical = xcd_remap(blockIdx.x, p.hkv * n_kt);
   const int g = logical / n_kt;
   const int kt = logical % n_kt;  // earlier keys (seen by more queries) first
   const int64_t lq = p.qm.len, lk = p.km.len;
@@ -231,33 +404,24 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(StepParams p, int n_kt
   const int64_t wkey0 = key0 + wave * 32;
   const int64_t mykey = wkey0 + l32;
   const bool key_ok = mykey < lk;
-  const int64_t kpos = key_ok ? seg_pos(p.km, mykey) : INT64_MAX;
+  // first query position that sees this lane's key (never, for a missing key)
+  const int kmin = !key_ok ? INT_MAX : (p.causal ? (int)seg_pos(p.km, mykey) : INT_MIN);
   int64_t gk_lo, gk_hi, wk_lo = INT64_MAX, wk_hi = INT64_MIN;
   seg_bounds(p.km, key0, key1, gk_lo, gk_hi);
   const bool wave_has_keys = wkey0 < lk;
   if (wave_has_keys) seg_bounds(p.km, wkey0, wkey0 + 32 < lk ? wkey0 + 32 : lk, wk_lo, wk_hi);
 
-  const bf16_t* Kg = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
-  const bf16_t* Vg = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
-
-  // K^T / V^T as B operands: lane = key column, d = 16c + 8*hi .. +8
   bf16x8 kreg[NC], vreg[NC];
+  {
+    const bf16_t* Kp = (const bf16_t*)p.k + (int64_t)g * p.k_hs + mykey * p.k_ss + 8 * hi;
+    const bf16_t* Vp = (const bf16_t*)p.v + (int64_t)g * p.v_hs + mykey * p.v_ss + 8 * hi;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    bf16x8 z = {};
-    kreg[c] = key_ok ? *(const bf16x8*)(Kg + mykey * p.k_ss + 16 * c + 8 * hi) : z;
-    vreg[c] = key_ok ? *(const bf16x8*)(Vg + mykey * p.v_ss + 16 * c + 8 * hi) : z;
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 z = {};
+      kreg[c] = key_ok ? *(const bf16x8*)(Kp + 16 * c) : z;
+      vreg[c] = key_ok ? *(const bf16x8*)(Vp + 16 * c) : z;
+    }
   }
-  // K tile in LDS (row-major) for dQ = dS K
-#pragma unroll
-  for (int i = 0; i < NLK; ++i) {
-    const int c = i * 256 + tid;
-    const int r = c / CPR, col = (c % CPR) * 8;
-    const int64_t key = key0 + r;
-    bf16x8 z = {};
-    *(bf16x8*)(sK + r * KSTR + col) = key < lk ? *(const bf16x8*)(Kg + key * p.k_ss + col) : z;
-  }
-
   f32x16 dkacc[ND], dvacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
@@ -282,35 +446,37 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(StepParams p, int n_kt
     return it;
   };
 
-  bf16x8 qr[NLQ], dr[NLQ];
-  auto load_regs = [&](int it) {
+  RowStage<QT, D, QSTR> qs, ds;
+  ColStage<QT, D, QTSTR> qts, dts;
+  qs.init(p.q_ss, tid);
+  ds.init(p.do_ss, tid);
+  if (QTT) {
+    qts.init(p.q_ss, tid);
+    dts.init(p.do_ss, tid);
+  }
+  auto load = [&](int it) {
     const int h = g * p.group + it / n_qt;
     const int64_t q0 = (int64_t)(it % n_qt) * QT;
     const bf16_t* Qh = (const bf16_t*)p.q + (int64_t)h * p.q_hs;
-    const bf16_t* Dh = (const bf16_t*)p.dout + (int64_t)h * p.do_hs;
-#pragma unroll
-    for (int i = 0; i < NLQ; ++i) {
-      const int c = i * 256 + tid;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      const int64_t row = q0 + r;
-      bf16x8 z = {};
-      qr[i] = row < lq ? *(const bf16x8*)(Qh + row * p.q_ss + col) : z;
-      dr[i] = row < lq ? *(const bf16x8*)(Dh + row * p.do_ss + col) : z;
+    const bf16_t* Gh = (const bf16_t*)p.dout + (int64_t)h * p.do_hs;
+    qs.load(Qh, p.q_ss, q0, lq);
+    ds.load(Gh, p.do_ss, q0, lq);
+    if (QTT) {
+      qts.load(Qh, p.q_ss, q0, lq);
+      dts.load(Gh, p.do_ss, q0, lq);
     }
   };
-
-  int it = p.hkv > 0 && lq > 0 ? next_visible(0) : n_it;
-  if (it < n_it) load_regs(it);
+  int it = lq > 0 ? next_visible(0) : n_it;
+  if (it < n_it) load(it);
   while (it < n_it) {
     const int h = g * p.group + it / n_qt;
     const int64_t q0 = (int64_t)(it % n_qt) * QT;
-    __syncthreads();  // previous iteration finished with sQ, sdO, sdsT, sL
-#pragma unroll
-    for (int i = 0; i < NLQ; ++i) {
-      const int c = i * 256 + tid;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      *(bf16x8*)(sQ + r * QSTR + col) = qr[i];
-      *(bf16x8*)(sdO + r * QSTR + col) = dr[i];
+    __syncthreads();
+    qs.store(sQ);
+    ds.store(sdO);
+    if (QTT) {
+      qts.store(sQt);
+      dts.store(sdOt);
     }
     if (tid < QT) {
       const int64_t row = q0 + tid;
@@ -325,105 +491,58 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(StepParams p, int n_kt
     }
     __syncthreads();
     const int itn = next_visible(it + 1);
-    if (itn < n_it) load_regs(itn);
+    if (itn < n_it) load(itn);
 
     int64_t tq_lo, tq_hi;
     tile_bounds(it, tq_lo, tq_hi);
     const bool wave_skip = !wave_has_keys || (p.causal && tq_hi < wk_lo);
-    if (wave_skip) {
-      // no visible pair for this wave's keys: its dS columns are zero
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x4 z = {};
-          *(bf16x4*)(sdsT + (wave * 32 + l32) * SSTR + qb * 32 + 8 * i + 4 * hi) = z;
-        }
-    } else {
-      const bool need_mask = !key_ok || (int64_t)(q0 + QT) > lq || (p.causal && wk_hi > tq_lo) ||
-                             (wkey0 + 32 > lk);
-      f32x16 sacc[2], pacc[2];
+    if (!wave_skip) {
+      const bool need_mask = (wkey0 + 32 > lk) || q0 + QT > lq || (p.causal && wk_hi > tq_lo);
+      const TilePos tp(p.qm, q0, QT);
+      // one 32-query block at a time: S, dP -> P, dS -> dV^T, dK^T updates
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
-      }
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bf16x8 aq = *(const bf16x8*)(sQ + (qb * 32 + l32) * QSTR + 16 * c + 8 * hi);
-          const bf16x8 ao = *(const bf16x8*)(sdO + (qb * 32 + l32) * QSTR + 16 * c + 8 * hi);
-          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[c], sacc[qb], 0, 0, 0);
-          pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[c], pacc[qb], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) {
+          const int off = (qb * 32 + srow) * QSTR + 16 * c + 8 * hi;
+          sacc = mfma32(*(const bf16x8*)(sQ + off), kreg[c], sacc);
+          pacc = mfma32(*(const bf16x8*)(sdO + off), vreg[c], pacc);
         }
-      }
-      // P and dS (lanes = keys, registers = queries 8*(r/4) + 4*hi + r%4)
-      bf16x8 pP[2][2], pS[2][2];
+        // register r is query q0 + qb*32 + 16*(r/8) + 8*hi + r%8
+        bf16x8 pP[2], pS[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+        for (int hf = 0; hf < 2; ++hf) {
+          const int qo = qb * 32 + 16 * hf + 8 * hi;
+          const f32x4 la = *(const f32x4*)(sL + qo), lb = *(const f32x4*)(sL + qo + 4);
+          const f32x4 da = *(const f32x4*)(sDl + qo), db_ = *(const f32x4*)(sDl + qo + 4);
+          bf16x8 p8, s8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qrow = qb * 32 + 8 * i + 4 * hi;
-          const f32x4 l4 = *(const f32x4*)(sL + qrow);
-          const f32x4 d4 = *(const f32x4*)(sDl + qrow);
-          bf16x4 ds4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * i + j;
-            float pr = __builtin_amdgcn_exp2f(sacc[qb][r] * p.scale_log2 - l4[j]);
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            const float l2 = e < 4 ? la[e] : lb[e - 4];
+            const float dl = e < 4 ? da[e] : db_[e - 4];
+            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -l2));
             if (need_mask) {
-              const int64_t row = q0 + qrow + j;
-              const bool vis = key_ok && row < lq && (!p.causal || kpos <= seg_pos(p.qm, row));
+              const bool vis = (qo + e < tp.nvalid) & (tp.pos(qo + e) >= kmin);
               pr = vis ? pr : 0.f;
             }
-            const float ds = pr * (pacc[qb][r] - d4[j]);
-            pP[qb][i >> 1][(i & 1) * 4 + j] = (bf16_t)pr;
-            const bf16_t dsb = (bf16_t)ds;
-            pS[qb][i >> 1][(i & 1) * 4 + j] = dsb;
-            ds4[j] = dsb;
+            p8[e] = (bf16_t)pr;
+            s8[e] = (bf16_t)(pr * (pacc[r] - dl));
           }
-          *(bf16x4*)(sdsT + (wave * 32 + l32) * SSTR + qrow) = ds4;
+          pP[hf] = p8;
+          pS[hf] = s8;
         }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (contraction over the 64 queries)
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
+        for (int db = 0; db < ND; ++db) {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16x8 ao = tr_operand(sdO, QSTR, 16 * cc + tr_row, 32 * db + tr_col);
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pP[cc >> 1][cc & 1], dvacc[db], 0, 0, 0);
-          const bf16x8 aq = tr_operand(sQ, QSTR, 16 * cc + tr_row, 32 * db + tr_col);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pS[cc >> 1][cc & 1], dkacc[db], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // all dS columns in LDS
-    // dQ tile = dS (64 q x 128 keys) K (128 keys x D); wave -> (query block, d blocks)
-    {
-      const int qb = wave >> 1;
-      f32x16 qacc[NDW];
-#pragma unroll
-      for (int j = 0; j < NDW; ++j) qacc[j] = f32x16{};
-      const int kc_end = (int)((key1 - key0 + 15) / 16);
-      for (int kc = 0; kc < kc_end; ++kc) {
-        const bf16x8 a = tr_operand(sdsT, SSTR, 16 * kc + tr_row, qb * 32 + tr_col);
-#pragma unroll
-        for (int j = 0; j < NDW; ++j) {
-          const int db = (wave & 1) * NDW + j;
-          const bf16x8 b = tr_operand(sK, KSTR, 16 * kc + tr_row, 32 * db + tr_col);
-          qacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, qacc[j], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NDW; ++j) {
-        const int db = (wave & 1) * NDW + j;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = q0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < lq)
-            unsafeAtomicAdd(p.o + row * p.o_ss + (int64_t)h * p.o_hs + 32 * db + l32,
-                            qacc[j][r] * p.scale);
+          for (int hf = 0; hf < 2; ++hf) {
+            const int cc = 2 * qb + hf;
+            const bf16x8 ao = rows_operand<QTT, QSTR, QTSTR>(sdO, sdOt, 16 * cc, 32 * db, lane);
+            dvacc[db] = mfma32(ao, pP[hf], dvacc[db]);
+            const bf16x8 aq = rows_operand<QTT, QSTR, QTSTR>(sQ, sQt, 16 * cc, 32 * db, lane);
+            dkacc[db] = mfma32(aq, pS[hf], dkacc[db]);
+          }
         }
       }
     }
@@ -455,6 +574,15 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(StepParams p, int n_kt
     }
 }
 
+int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
 template <int D, typename T>
 hipError_t launch_simple(const StepParams& p, hipStream_t s) {
   constexpr int RPB = 64 / (D / 64);
@@ -469,10 +597,19 @@ hipError_t launch_simple(const StepParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
+  if (p.qm.len > 0 && p.km.len > 0) {
+    const int hpw = gcd_int(p.group, 4);
+    const int rows_per_wg = (4 / hpw) * 32;
+    const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
+    const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, (bool)RA_BWD_KTT>), dim3((unsigned)grid), dim3(256), 0, s,
+                       p, hpw, n_qt, rows_per_wg);
+  }
   const int n_kt = (int)((p.km.len + 127) / 128);
   const int64_t grid = (int64_t)p.hkv * n_kt;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_mfma_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, p, n_kt);
+  if (grid > 0)
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, (bool)RA_BWD_QTT>), dim3((unsigned)grid), dim3(256), 0, s,
+                       p, n_kt);
   return hipGetLastError();
 }
 

@@ -4,22 +4,33 @@
 // LoongTrain", "The Communication Overhead and Causal Imbalance of Ring
 // Attention"; scale 1/sqrt(d) and softmax(QK^T scale) V as in its "Step 3").
 //
-// bf16 path (gfx950 MFMA): a workgroup of 4 waves shares one KV head. Each wave
-// owns 32*QB query rows of one query head; the waves of a workgroup are the
-// grouped query heads that read the same K/V (GQA packing) and/or consecutive
-// row blocks. K/V tiles of 64 keys are staged in LDS; each wave computes
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that a lane owns one query
-// column: the row max/sum of the online softmax are in-lane plus one exchange
-// with the other half-wave. exp2(S^T - m) is rounded to bf16 and used in place
-// as the B operand of O^T += V^T P^T; V^T comes from LDS through the
-// transposing read ds_read_b64_tr_b16. Tiles whose keys are all later than the
-// workgroup's queries are skipped; fully visible tiles run without masking.
+// bf16 path (gfx950 MFMA): a workgroup of 4 waves shares one KV head; two
+// workgroups share a CU (two waves per SIMD). Each wave owns 32 query rows of
+// one query head; the waves of a workgroup are the grouped query heads that
+// read the same K/V (GQA packing) and/or consecutive row blocks. Per 64-key
+// tile, K is staged in LDS row-major and V transposed (V^T[d][key], built by
+// register shuffles). Each wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 so that a lane owns one query column: the online
+// softmax row max/sum are in-lane plus one exchange with the other half-wave.
+// K rows are fed in the sigma order (ra_tile.h), so each 8-register chunk of
+// exp2(S^T - m) covers 8 consecutive keys and, rounded to bf16, is directly the
+// B operand of O^T += V^T P^T, whose A operand is one 16-byte LDS read of V^T.
+// Tiles whose keys are all later than the workgroup's queries are skipped;
+// fully visible tiles run without masking; O is rescaled only when a row max
+// moved.
 //
 // fp32 path: a plain VALU kernel (one or two lanes per query row), used for the
 // fp32 workload and kept deliberately simple.
+#include <limits.h>
 #include <math.h>
 
 #include "ra_internal.h"
+#include "ra_tile.h"
+
+// minimum resident workgroups per CU (2: two waves per SIMD hide latency)
+#ifndef RA_FWD_MINB
+#define RA_FWD_MINB 2
+#endif
 
 namespace {
 
@@ -98,77 +109,68 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 }
 
 // ============================================================= MFMA kernel
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ inline bf16x4 ds_read_tr(const bf16_t* lds_ptr) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-template <int D, int QB>
-__global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
-                                                          int rows_per_wg) {
-  constexpr int KT = 64;         // keys per LDS tile
-  constexpr int KSTR = D + 8;    // LDS row strides (elements), chosen against bank conflicts
-  constexpr int VSTR = D + 16;
-  constexpr int NC = D / 16;     // 16-wide d chunks (QK^T contraction steps)
-  constexpr int ND = D / 32;     // 32-wide d blocks of O^T
-  constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
-  constexpr int NLD = KT * CPR / 256;
+// VT selects how V^T reaches the O^T += V^T P^T product: true = V staged
+// transposed in LDS (register transpose, one 16-byte read per operand),
+// false = V staged row-major and read with ds_read_b64_tr_b16.
+template <int D, bool VT>
+__global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
+                                                                    int rows_per_wg) {
+  constexpr int KT = 64;          // keys per LDS tile
+  constexpr int KSTR = D + 8;     // sK row stride (elements)
+  constexpr int VSTR = VT ? KT + 8 : D + 16;  // V^T rows are d (VT) or V rows are keys
+  constexpr int VROWS = VT ? D : KT;
+  constexpr int NC = D / 16;      // 16-wide d chunks (QK^T contraction steps)
+  constexpr int ND = D / 32;      // 32-wide d blocks of O^T
   __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[KT * VSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[VROWS * VSTR];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int l32 = lane & 31, hi = lane >> 5;
+  const int srow = sigma32(l32);
 
-  // ---- workgroup -> (KV head, head subgroup, query tile); same-KV-head tiles
-  // are placed on the same XCD (workgroups go round-robin over the 8 XCDs).
+  // ---- workgroup -> (KV head, head subgroup, query tile); tiles of one KV head
+  // share an XCD (and its L2); later (heavier) query tiles start first.
   const int nsub = p.group / hpw;
   const int total = p.hkv * nsub * n_qt;
-  const int w = blockIdx.x;
-  const int logical = (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
+  const int logical = xcd_remap(blockIdx.x, total);
   const int gh = logical / n_qt;
-  const int qt = n_qt - 1 - (logical % n_qt);  // later (heavier) rows first
+  const int qt = n_qt - 1 - (logical % n_qt);
   const int g = gh / nsub, hs = gh % nsub;
   const int h = g * p.group + hs * hpw + (wave % hpw);
   const int64_t lq = p.qm.len, lk = p.km.len;
   const int64_t wg_r0 = (int64_t)qt * rows_per_wg;
-  const int64_t row0 = wg_r0 + (int64_t)(wave / hpw) * 32 * QB;
+  const int64_t row0 = wg_r0 + (int64_t)(wave / hpw) * 32;
 
   int64_t wq_lo = 0, wq_hi = -1, gq_lo, gq_hi;
   const bool wave_active = row0 < lq;
-  if (wave_active) seg_bounds(p.qm, row0, row0 + 32 * QB < lq ? row0 + 32 * QB : lq, wq_lo, wq_hi);
+  if (wave_active) seg_bounds(p.qm, row0, row0 + 32 < lq ? row0 + 32 : lq, wq_lo, wq_hi);
   seg_bounds(p.qm, wg_r0, wg_r0 + rows_per_wg < lq ? wg_r0 + rows_per_wg : lq, gq_lo, gq_hi);
 
-  const bf16_t* Q = (const bf16_t*)p.q;
   const bf16_t* K = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
   const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
 
   // Q^T as the B operand: lane holds query column l32, d = 16c + 8*hi .. +8
-  bf16x8 qreg[QB][NC];
-  int qpos[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int64_t row = row0 + qb * 32 + l32;
-    const bool ok = row < lq;
-    qpos[qb] = ok ? (int)seg_pos(p.qm, row) : -1;
+  bf16x8 qreg[NC];
+  const int64_t qrow = row0 + l32;
+  const bool qok = qrow < lq;
+  const int qpos = qok ? (int)seg_pos(p.qm, qrow) : -1;
+  const int qlim = (p.causal || !qok) ? qpos : INT_MAX;  // last visible key position
+  {
+    const bf16_t* Q = (const bf16_t*)p.q + qrow * p.q_ss + (int64_t)h * p.q_hs + 8 * hi;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 z = {};
-      qreg[qb][c] = ok ? *(const bf16x8*)(Q + row * p.q_ss + (int64_t)h * p.q_hs + 16 * c + 8 * hi) : z;
+      qreg[c] = qok ? *(const bf16x8*)(Q + 16 * c) : z;
     }
   }
 
-  f32x16 oacc[QB][ND];
-  float m_run[QB], l_run[QB];
+  f32x16 oacc[ND];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[qb][db] = f32x16{};
-  }
+  for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;  // running max, scaled (log2) units
+  float l_run = 0.f;        // running sum of this half-wave's keys
 
   const int n_kt = (int)((lk + KT - 1) / KT);
   auto tile_bounds = [&](int t, int64_t& lo, int64_t& hi_) {
@@ -186,118 +188,106 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     return t;
   };
 
-  bf16x8 kr[NLD], vr[NLD];
-  auto load_regs = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c = i * 256 + tid;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      const int64_t key = (int64_t)t * KT + r;
-      bf16x8 z = {};
-      kr[i] = key < lk ? *(const bf16x8*)(K + key * p.k_ss + col) : z;
-      vr[i] = key < lk ? *(const bf16x8*)(V + key * p.v_ss + col) : z;
-    }
-  };
-  auto store_lds = [&]() {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c = i * 256 + tid;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      *(bf16x8*)(sK + r * KSTR + col) = kr[i];
-      *(bf16x8*)(sV + r * VSTR + col) = vr[i];
-    }
-  };
-
-  // transposing-read lane roles (see ds_read_tr): 16-lane group grp, member i
+  // lane roles of the transposing read (VT == false)
   const int grp = lane >> 4, gi = lane & 15;
-  const int tr_key = 4 * (grp >> 1) + (gi >> 2);  // + 16*chunk (+8 for the 2nd read)
-  const int tr_d = 16 * (grp & 1) + 4 * (gi & 3);   // + 32*db
+  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
+
+  RowStage<KT, D, KSTR> ks;
+  ks.init(p.k_ss, tid);
+  RowStage<KT, D, VSTR> vs_rows;
+  ColStage<KT, D, VSTR> vs_cols;
+  if (VT) vs_cols.init(p.v_ss, tid); else vs_rows.init(p.v_ss, tid);
+  auto load_tile = [&](int t) {
+    ks.load(K, p.k_ss, (int64_t)t * KT, lk);
+    if (VT) vs_cols.load(V, p.v_ss, (int64_t)t * KT, lk);
+    else vs_rows.load(V, p.v_ss, (int64_t)t * KT, lk);
+  };
 
   int t = next_visible(0);
-  if (t < n_kt) load_regs(t);
+  if (t < n_kt) load_tile(t);
   while (t < n_kt) {
     __syncthreads();
-    store_lds();
+    ks.store(sK);
+    if (VT) vs_cols.store(sV); else vs_rows.store(sV);
     __syncthreads();
     const int tn = next_visible(t + 1);
-    if (tn < n_kt) load_regs(tn);
+    if (tn < n_kt) load_tile(tn);
 
     int64_t klo, khi;
     tile_bounds(t, klo, khi);
     const bool wave_skip = !wave_active || (p.causal && klo > wq_hi);
     if (!wave_skip) {
-      const bool ragged = (int64_t)(t + 1) * KT > lk;
-      const bool need_mask = ragged || (p.causal && khi > wq_lo);
-      // ---- S^T = K Q^T : two 32-key blocks x QB 32-query blocks
-      f32x16 sacc[2][QB];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16{};
+      const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
+      // ---- S^T = K Q^T (rows of K in sigma order)
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * KSTR + 16 * c + 8 * hi);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], sacc[kb][qb], 0, 0, 0);
+          const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + srow) * KSTR + 16 * c + 8 * hi);
+          sacc[kb] = mfma32(a, qreg[c], sacc[kb]);
         }
       }
-      // ---- scale, mask, online softmax (exp2 domain)
-      bf16x8 pk[2][QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
+      // register r of key block kb is key t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
+      if (need_mask) {
+        const TilePos tp(p.km, (int64_t)t * KT, KT);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float s = sacc[kb][qb][r] * p.scale_log2;
-            if (need_mask) {
-              const int64_t key = (int64_t)t * KT + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              const bool vis = key < lk && (!p.causal || seg_pos(p.km, key) <= qpos[qb]);
-              s = vis ? s : -INFINITY;
-            }
-            sacc[kb][qb][r] = s;
-            mx = fmaxf(mx, s);
+            const int off = kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+            const bool vis = (off < tp.nvalid) & (tp.pos(off) <= qlim);
+            sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-        m_run[qb] = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            bf16x8 v8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pe = __builtin_amdgcn_exp2f(sacc[kb][qb][hf * 8 + e] - m_use);
-              rs += pe;
-              v8[e] = (bf16_t)pe;
-            }
-            pk[kb][qb][hf] = v8;
-          }
-        l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[qb][db] *= alpha;
       }
-      // ---- O^T += V^T P^T : V^T (d x 16 keys) by transposing LDS reads
+      // ---- online softmax in the exp2 domain; max taken on raw scores (scale > 0)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * p.scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      bf16x8 pk[2][2];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          bf16x8 v8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * hf + e], p.scale_log2, -m_use));
+            rs += pe;
+            v8[e] = (bf16_t)pe;
+          }
+          pk[kb][hf] = v8;
+        }
+      l_run = l_run * alpha + rs;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+      }
+      // ---- O^T += V^T P^T: lane half hi takes keys 16*cc + 8*hi .. +8
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const bf16_t* base = sV + (16 * cc + tr_key) * VSTR + 32 * db + tr_d;
-          const bf16x4 lo4 = ds_read_tr(base);
-          const bf16x4 hi4 = ds_read_tr(base + 8 * VSTR);
-          const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[cc >> 1][qb][cc & 1],
-                                                                   oacc[qb][db], 0, 0, 0);
+          bf16x8 a;
+          if (VT) {
+            a = *(const bf16x8*)(sV + (32 * db + l32) * VSTR + 16 * cc + 8 * hi);
+          } else {
+            // keys 16cc + 4*(grp>>1) + e and +8: the order pk uses is
+            // {8hi + 0..7}; read rows 16cc + 8hi + {0..3, 4..7} instead
+            const bf16_t* base = sV + (16 * cc + 8 * hi + (gi >> 2)) * VSTR + 32 * db + tr_col;
+            const bf16x4 lo4 = ds_read_tr(base);
+            const bf16x4 hi4 = ds_read_tr(base + 4 * VSTR);
+            a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          oacc[db] = mfma32(a, pk[cc >> 1][cc & 1], oacc[db]);
         }
       }
     }
@@ -306,25 +296,21 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(StepParams p, int hpw,
 
   // ---- epilogue: normalise, write O_step [row][h][d] and LSE_step [h][row]
   if (!wave_active) return;
+  const float ltot = l_run + __shfl_xor(l_run, 32);
+  if (qok) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float* orow = p.o + qrow * p.o_ss + (int64_t)h * p.o_hs;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const int64_t row = row0 + qb * 32 + l32;
-    if (row < lq) {
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      float* orow = p.o + row * p.o_ss + (int64_t)h * p.o_hs;
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int i = 0; i < 4; ++i) {
+        f32x4 v4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 v4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v4[j] = oacc[qb][db][4 * i + j] * inv;
-          *(f32x4*)(orow + 32 * db + 8 * i + 4 * hi) = v4;
-        }
-      if (hi == 0)
-        p.lse_out[(int64_t)h * lq + row] = ltot > 0.f ? (m_run[qb] + log2f(ltot)) * kLn2 : -INFINITY;
-    }
+        for (int j = 0; j < 4; ++j) v4[j] = oacc[db][4 * i + j] * inv;
+        *(f32x4*)(orow + 32 * db + 8 * i + 4 * hi) = v4;
+      }
+    if (hi == 0)
+      p.lse_out[(int64_t)h * lq + qrow] = ltot > 0.f ? (m_run + log2f(ltot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -337,16 +323,20 @@ int gcd_int(int a, int b) {
   return a;
 }
 
-template <int D, int QB>
+#ifndef RA_FWD_VT
+#define RA_FWD_VT 1
+#endif
+
+template <int D>
 hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   const int hpw = gcd_int(p.group, 4);
   const int rb = 4 / hpw;
-  const int rows_per_wg = rb * 32 * QB;
+  const int rows_per_wg = rb * 32;
   const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
   const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, QB>), dim3((unsigned)grid), dim3(256), 0, s, p, hpw, n_qt,
-                     rows_per_wg);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, (bool)RA_FWD_VT>), dim3((unsigned)grid), dim3(256), 0, s, p,
+                     hpw, n_qt, rows_per_wg);
   return hipGetLastError();
 }
 
@@ -362,8 +352,8 @@ hipError_t launch_simple(const StepParams& p, hipStream_t s) {
 
 hipError_t launch_step_fwd(const StepParams& p, int dtype, int head_dim, hipStream_t s) {
   if (dtype == RA_BF16) {
-    if (head_dim == 128) return launch_mfma<128, 1>(p, s);
-    return launch_mfma<64, 1>(p, s);
+    if (head_dim == 128) return launch_mfma<128>(p, s);
+    return launch_mfma<64>(p, s);
   }
   if (head_dim == 128) return launch_simple<128, float>(p, s);
   return launch_simple<64, float>(p, s);

@@ -1,0 +1,167 @@
+// Device helpers shared by the MFMA attention kernels (gfx950, wave64).
+//
+// MFMA v_mfma_f32_32x32x16_bf16 lane layouts (verified on gfx950):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +8
+//   B (16 x 32): lane l holds col l%32, k = 8*(l/32) .. +8
+//   C (32 x 32): lane l holds col l%32, register r is row 8*(r/4) + 4*(l/32) + r%4
+//
+// Row permutation sigma (swap bits 2 and 3 of a 0..31 row index): if the A
+// operand of a product C = A B is loaded with lane l32 holding logical row
+// sigma(l32), then C register r of lane half hi is logical row
+// 16*(r/8) + 8*hi + r%8. Registers 0..7 (and 8..15) of a lane then cover 8
+// CONSECUTIVE logical rows, so C can be reused directly as the B operand of a
+// product that contracts over those rows, with the other operand read from a
+// transposed LDS tile by one 16-byte load.
+#pragma once
+#include "ra_internal.h"
+
+__device__ __forceinline__ int sigma32(int l32) {
+  return (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Registers 8*half .. 8*half+7 of an accumulator, rounded to bf16.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16_t)x[8 * half + e];
+  return r;
+}
+
+// Transpose a 4-row x 8-column bf16 block held as four 8-wide rows into eight
+// 4-wide columns (column e = {row0[e], row1[e], row2[e], row3[e]}).
+__device__ __forceinline__ void transpose4x8(const bf16x8 (&in)[4], bf16x4 (&out)[8]) {
+  typedef __attribute__((__vector_size__(16 * sizeof(__bf16)))) __bf16 bf16x16;
+  const bf16x16 p01 = __builtin_shufflevector(in[0], in[1], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5,
+                                              13, 6, 14, 7, 15);
+  const bf16x16 p23 = __builtin_shufflevector(in[2], in[3], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5,
+                                              13, 6, 14, 7, 15);
+  out[0] = __builtin_shufflevector(p01, p23, 0, 1, 16, 17);
+  out[1] = __builtin_shufflevector(p01, p23, 2, 3, 18, 19);
+  out[2] = __builtin_shufflevector(p01, p23, 4, 5, 20, 21);
+  out[3] = __builtin_shufflevector(p01, p23, 6, 7, 22, 23);
+  out[4] = __builtin_shufflevector(p01, p23, 8, 9, 24, 25);
+  out[5] = __builtin_shufflevector(p01, p23, 10, 11, 26, 27);
+  out[6] = __builtin_shufflevector(p01, p23, 12, 13, 28, 29);
+  out[7] = __builtin_shufflevector(p01, p23, 14, 15, 30, 31);
+}
+
+// ---- global -> register staging through buffer loads. A buffer descriptor
+// spans the rows [row0, nrows) of one head (row stride ss elements); reads past
+// its end return zeros, so ragged tails need no selects. The descriptor is
+// built per tile from uniform values (scalar arithmetic), and each thread's
+// byte offsets inside a tile are fixed, so a load costs no vector ALU work.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16_t* base, int64_t ss,
+                                                            int64_t row0, int64_t nrows) {
+  int64_t bytes = (nrows - row0) * ss * 2;
+  bytes = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * ss), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Row-major staging of a T x D bf16 tile into lds[row * STR + col]: 16-byte
+// chunk c (stride 256 over the workgroup) is row c / (D/8), column
+// 8*(c % (D/8)), so every wave writes whole rows (conflict-free stores).
+template <int T, int D, int STR>
+struct RowStage {
+  static constexpr int CPR = D / 8;
+  static constexpr int N = T * CPR / 256;
+  static_assert(N >= 1 && T * CPR % 256 == 0, "tile must be a multiple of 256 chunks");
+  uint32_t voff[N];
+  int lds0;
+  bf16x8 v[N];
+  __device__ __forceinline__ void init(int64_t ss, int tid) {
+    const int row = tid / CPR, col = 8 * (tid % CPR);
+    lds0 = row * STR + col;
+#pragma unroll
+    for (int i = 0; i < N; ++i) voff[i] = (uint32_t)(((row + i * (256 / CPR)) * ss + col) * 2);
+  }
+  __device__ __forceinline__ void load(const bf16_t* base, int64_t ss, int64_t row0,
+                                       int64_t nrows) {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = buf_load16(r, voff[i]);
+  }
+  __device__ __forceinline__ void store(bf16_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) *(bf16x8*)(lds + lds0 + i * (256 / CPR) * STR) = v[i];
+  }
+};
+
+// Transposed staging of a T x D bf16 tile into lds[col * STR + row]: thread
+// c < (T/4)*(D/8) loads rows 4*(c % (T/4)) .. +3 at columns 8*(c / (T/4)) .. +8
+// and writes eight 4-row columns (64-bit stores) after a register transpose.
+template <int T, int D, int STR>
+struct ColStage {
+  static constexpr int RG = T / 4;
+  static constexpr int NTH = RG * (D / 8);
+  static_assert(NTH <= 256 && NTH % 64 == 0, "one pass of whole waves");
+  uint32_t voff0, vstep;
+  int lds0;
+  bool active;
+  bf16x8 v[4];
+  __device__ __forceinline__ void init(int64_t ss, int tid) {
+    active = tid < NTH;
+    const int rg = tid % RG, col = 8 * (tid / RG);
+    voff0 = (uint32_t)((4 * rg * ss + col) * 2);
+    vstep = (uint32_t)(ss * 2);
+    lds0 = col * STR + 4 * rg;
+  }
+  __device__ __forceinline__ void load(const bf16_t* base, int64_t ss, int64_t row0,
+                                       int64_t nrows) {
+    if (!active) return;
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = buf_load16(r, voff0 + j * vstep);
+  }
+  __device__ __forceinline__ void store(bf16_t* lds) const {
+    if (!active) return;
+    bf16x4 t[8];
+    transpose4x8(v, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *(bf16x4*)(lds + lds0 + e * STR) = t[e];
+  }
+};
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i of
+// the four 8-byte rows addressed by lanes 4e + (i/4) (e = 0..3), i.e. a 4x16
+// block read transposed. With lane roles (tr_row, tr_col) below, the pair of
+// reads at rows R and R+8 gives the 8-value MFMA operand of column C.
+__device__ __forceinline__ bf16x4 ds_read_tr(const bf16_t* lds_ptr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Branch-free key/query positions of one tile of rows [t0, t0 + n): when the
+// tile lies inside one segment, row t0 + off is at base + off. Positions fit in
+// int32 (checked on the host).
+struct TilePos {
+  int base, nvalid;
+  bool one_seg;
+  const SegMap* m;
+  int64_t t0;
+  __device__ __forceinline__ TilePos(const SegMap& map, int64_t start, int n) : m(&map), t0(start) {
+    one_seg = (start + n <= map.seg_len) || (start >= map.seg_len);
+    base = (int)seg_pos(map, start);
+    const int64_t left = map.len - start;
+    nvalid = left < n ? (int)left : n;
+  }
+  __device__ __forceinline__ int pos(int off) const {
+    return one_seg ? base + off : (int)seg_pos(*m, t0 + off);
+  }
+};
+
+// Workgroup id -> logical id that keeps consecutive logical ids on one XCD
+// (the dispatcher places workgroup w on XCD w % 8).
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  return (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
+}

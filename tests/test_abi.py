@@ -89,6 +89,8 @@ def test_validation_accepts_good_descriptor():
     (dict(q_segments=((0, 1, 2), 64)), None),       # 3 segments: rejected by make_desc
     (dict(k_segments=((0, 448), -1)), B.RA_EINVAL),
     (dict(scale=float("nan")), B.RA_EINVAL),
+    (dict(scale=-0.1), B.RA_EINVAL),
+    (dict(scale=0.0), B.RA_EINVAL),
     (dict(causal=2), B.RA_EINVAL),
     (dict(q_strides=(1024, 100)), B.RA_EINVAL),     # heads overlap (head stride < d)
     (dict(q_strides=(1028, 128)), B.RA_EALIGN),     # rows not 16-byte aligned
