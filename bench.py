@@ -34,6 +34,33 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_sources_sha256():
+    """Hash of the HIP sources (identifies the kernels a counter profile was taken on)."""
+    import hashlib
+    d = os.path.join(ROOT, "ring_attention_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(cfg_name):
+    """HBM bytes per ring_attn_step_bwd launch from the committed counter summary,
+    or None when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{cfg_name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if kernel_sources_sha256() not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            return float(line.split(":")[1])
+    return None
+
+
 def make_inputs(cfg, rank):
     import torch
     from ring_attention_attn_amd import synth
@@ -93,6 +120,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0, help="ring rank whose share is timed")
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one head_permute of 1 GiB (a plain copy of known size) before the "
+                         "warmup, to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} is not supported "
@@ -112,6 +142,13 @@ def main():
         f"hkv={cfg.hkv} d={cfg.d} {cfg.dtype} rank={args.rank}")
     q, K, V, do = make_inputs(cfg, args.rank)
     ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d, cfg.dtype)
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(7)   # 1 GiB
+        dst = torch.empty_like(src)
+        binding.head_permute(src, dst, 1 << 17, 32, 128, 4, 2, 0)   # [131072][32][128] -> [4][...]
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy probe: head_permute of 1 GiB done")
     torch.cuda.synchronize()
     log("inputs resident; warmup")
     for _ in range(args.warmup):
@@ -197,7 +234,8 @@ def main():
         "lse_merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms else None,
         "roofline": {"bound": "mfma", "kernel": "ring_attn_step_bwd", "achieved": round(bwd_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(cfg.name)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
