@@ -99,54 +99,72 @@ def _sample_rows(b, n_rand, seed):
     return np.unique(np.concatenate([fixed, rng.integers(0, 2 * b, n_rand)]))
 
 
-@pytest.mark.parametrize("cfg_name", ["llama3_8b_cp8_128k"])
+FULL_SIZE = ["llama3_8b_cp8_128k", "llama3_70b_hp2_cp32_512k", "hp4_cp16_1m", "mha7b_hp8_cp8_1m"]
+
+
+@pytest.mark.parametrize("cfg_name", FULL_SIZE)
 def test_full_size_share_sampled(cfg_name):
-    """The benchmark's workload at full size and in its launch configuration.
+    """Each bf16 workload at full size, in the benchmark's launch configuration.
 
     Sampled query rows (both zigzag halves, tile edges) of several heads: O, LSE
     and dQ from the oracle row by row. Sampled late keys (the last 64 positions,
     seen only by this rank's last rows): dK and dV from the oracle. Identities
     over all keys: sum_k dV_k = sum of dO over the group's rows and heads, and
-    sum_k dK_k = 0."""
+    sum_k dK_k = 0. For the 2D-Attention workload the local queries come from
+    the head permute of a [rows][32][128] tensor (destination group 0), as the
+    head-parallel all-to-all would deliver them."""
+    from ring_attention_attn_amd import binding as B
+    from ring_attention_attn_amd import synth
     cfg = CONFIGS[cfg_name]
     S, P, r, hq, hkv, d = cfg.S, cfg.P, 0, cfg.hq, cfg.hkv, cfg.d
     G = hq // hkv
     scale = 1 / math.sqrt(d)
+    print(f"[full-size] {cfg_name}: S={S} P={P} hq={hq} hkv={hkv}", flush=True)
     x = share_inputs(S, P, r, hq, hkv, d, "bf16", seed=cfg.seed)
-    _, got = run_share(S, cfg.inner, cfg.outer, r, hq, hkv, d, "bf16", x)
     b = S // (2 * P)
+    if cfg.permute_heads:
+        # Q of the share = head group 0 of the permuted [2b][H][d] tensor
+        H = cfg.permute_heads
+        pre = synth.blocks_tensor(cfg.seed, synth.T_QPRE, synth.paired_blocks(P, r), b, H, d, "bf16")
+        src = torch.from_numpy(pre.view(np.int16)).cuda()
+        dst = torch.empty((H // hq, 2 * b, hq, d), dtype=torch.int16, device="cuda")
+        B.head_permute(src, dst, 2 * b, H, d, H // hq, 2, 0)
+        torch.cuda.synchronize()
+        x["q"] = dst[0].cpu().numpy().view(np.uint16)
+        assert np.array_equal(x["q"], oracle.head_permute(pre, H // hq)[0])
+        del src, dst
+    _, got = run_share(S, cfg.inner, cfg.outer, r, hq, hkv, d, "bf16", x)
     pos = oracle.zigzag_positions(S, P, r)
-    rows = _sample_rows(b, 24, cfg.seed)
-    for h in (0, G - 1, hq // 2 + 1, hq - 1):
+    rows = _sample_rows(b, 16, cfg.seed)
+    heads = sorted({0, G - 1, hq // 2, hq - 1})
+    for h in heads:
         g = h // G
         kg = widen(x["k_nat"][:, g:g + 1], "bf16")
         vg = widen(x["v_nat"][:, g:g + 1], "bf16")
         qr = widen(x["q"][rows][:, h:h + 1], "bf16")
         dor = widen(x["do"][rows][:, h:h + 1], "bf16")
-        res = oracle.share_backward(qr, kg, vg, dor, pos[rows], scale)
+        res = oracle.share_backward(qr, kg, vg, dor, pos[rows], scale, row_block=16)
         assert_close(f"O h{h}", got["O"][rows][:, h:h + 1], res["O"], "bf16")
         assert_close(f"LSE h{h}", got["LSE"][h:h + 1, rows], res["LSE"], "bf16", is_lse=True)
         assert_close(f"dQ h{h}", got["dQ"][rows][:, h:h + 1], res["dQ"], "bf16")
     # late keys: positions S-64 .. S-1 = chunk 0's back block tail
     key_pos = np.arange(S - 64, S)
     key_rows = b + (key_pos - (2 * P - 1) * b)          # rows of chunk 0 (and of this rank)
-    for g in (0, hkv - 1):
-        heads = slice(g * G, (g + 1) * G)
+    for g in sorted({0, hkv - 1}):
+        hs_ = slice(g * G, (g + 1) * G)
         kg = widen(x["k_nat"][:, g:g + 1], "bf16")
         vg = widen(x["v_nat"][:, g:g + 1], "bf16")
-        qr = widen(x["q"][key_rows][:, heads], "bf16")
-        dor = widen(x["do"][key_rows][:, heads], "bf16")
-        fw = oracle.share_backward(qr, kg, vg, dor, pos[key_rows], scale)
+        qr = widen(x["q"][key_rows][:, hs_], "bf16")
+        dor = widen(x["do"][key_rows][:, hs_], "bf16")
+        fw = oracle.share_backward(qr, kg, vg, dor, pos[key_rows], scale, row_block=16)
         _, dk, dv = oracle.step_backward(qr, kg[key_pos], vg[key_pos], dor, fw["LSE"], fw["D"],
                                          pos[key_rows], key_pos, scale)
         assert_close(f"dK late g{g}", got["dK"][0][key_rows][:, g:g + 1], dk, "bf16")
         assert_close(f"dV late g{g}", got["dV"][0][key_rows][:, g:g + 1], dv, "bf16")
-    dk_all = got["dK"].astype(np.float64)
-    dv_all = got["dV"].astype(np.float64)
     do64 = widen(x["do"], "bf16")
     for g in range(hkv):
+        dv_sum = got["dV"][:, :, g].astype(np.float64).sum(axis=(0, 1))
         want_sum = do64[:, g * G:(g + 1) * G].sum(axis=(0, 1))
-        np.testing.assert_allclose(dv_all[:, :, g].sum(axis=(0, 1)), want_sum,
-                                   atol=1e-3 * np.abs(want_sum).max() + 1e-2)
-        s = dk_all[:, :, g].sum(axis=(0, 1))
-        assert np.abs(s).max() <= 1e-3 * np.abs(dk_all[:, :, g]).sum(axis=(0, 1)).max()
+        np.testing.assert_allclose(dv_sum, want_sum, atol=1e-3 * np.abs(want_sum).max() + 1e-2)
+        dk_g = got["dK"][:, :, g].astype(np.float64)
+        assert np.abs(dk_g.sum(axis=(0, 1))).max() <= 1e-3 * np.abs(dk_g).sum(axis=(0, 1)).max()
