@@ -22,6 +22,9 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     "-munsafe-fp-atomics",
+    # keep MFMA accumulators in VGPRs (the AGPR form made the dK/dV kernel copy
+    # its accumulators every iteration)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # packed fp32 VALU ops are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

@@ -28,6 +28,10 @@
 #ifndef RA_BWD_QTT
 #define RA_BWD_QTT 0
 #endif
+// 1: dK/dV kernel reads its K^T/V^T operands from LDS instead of registers
+#ifndef RA_BWD_KVL
+#define RA_BWD_KVL 0
+#endif
 
 namespace {
 
@@ -320,11 +324,21 @@ __global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 sacc = f32x16{}, pacc = f32x16{};
+        {
+          // chunk c+1's K and V operands load while chunk c's MFMAs run
+          bf16x8 ak[2], av[2];
+          auto ld = [&](int c, int slot) {
+            const int off = (kb * 32 + srow) * KSTR + 16 * c + 8 * hi;
+            ak[slot] = *(const bf16x8*)(sK + off);
+            av[slot] = *(const bf16x8*)(sV + off);
+          };
+          ld(0, 0);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int off = (kb * 32 + srow) * KSTR + 16 * c + 8 * hi;
-          sacc = mfma32(*(const bf16x8*)(sK + off), qreg[c], sacc);
-          pacc = mfma32(*(const bf16x8*)(sV + off), doreg[c], pacc);
+          for (int c = 0; c < NC; ++c) {
+            if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
+            sacc = mfma32(ak[c & 1], qreg[c], sacc);
+            pacc = mfma32(av[c & 1], doreg[c], pacc);
+          }
         }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -343,12 +357,17 @@ __global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams 
           dsk[kb][hf] = v8;
         }
       }
+      {
+        // step i = (db, cc); step i+1's K^T operand loads while step i's MFMA runs
+        bf16x8 a[2];
+        a[0] = rows_operand<KTT, KSTR, KTSTR>(sK, sKt, 0, 0, lane);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16x8 a = rows_operand<KTT, KSTR, KTSTR>(sK, sKt, 16 * cc, 32 * db, lane);
-          qacc[db] = mfma32(a, dsk[cc >> 1][cc & 1], qacc[db]);
+        for (int i = 0; i < 4 * ND; ++i) {
+          if (i + 1 < 4 * ND)
+            a[(i + 1) & 1] = rows_operand<KTT, KSTR, KTSTR>(sK, sKt, 16 * ((i + 1) & 3),
+                                                            32 * ((i + 1) >> 2), lane);
+          const int db = i >> 2, cc = i & 3;
+          qacc[db] = mfma32(a[i & 1], dsk[cc >> 1][cc & 1], qacc[db]);
         }
       }
     }
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams 
 //     dP = dO V^T put a key in each lane (query rows fed in sigma order), so P
 //     and dS, rounded to bf16, are directly the B operands of dV^T += dO^T P and
 //     dK^T += Q^T dS. Each dK/dV element has one writer.
-template <int D, bool QTT>
+template <int D, bool QTT, bool KVL>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
   constexpr int KB = 128;
   constexpr int QT = 64;
@@ -388,6 +407,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   __shared__ __attribute__((aligned(16))) bf16_t sdOt[QTT ? D * QTSTR : 8];
   __shared__ __attribute__((aligned(16))) float sL[QT];
   __shared__ __attribute__((aligned(16))) float sDl[QT];
+  // KVL: the workgroup's 128 keys of K and V stay in LDS (row-major) and the
+  // B operands are read per use, which keeps vector registers free for
+  // in-flight operand loads
+  constexpr int KVSTR = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t sKk[KVL ? KB * KVSTR : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t sVv[KVL ? KB * KVSTR : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -411,17 +436,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   const bool wave_has_keys = wkey0 < lk;
   if (wave_has_keys) seg_bounds(p.km, wkey0, wkey0 + 32 < lk ? wkey0 + 32 : lk, wk_lo, wk_hi);
 
-  bf16x8 kreg[NC], vreg[NC];
-  {
+  bf16x8 kreg[KVL ? 1 : NC], vreg[KVL ? 1 : NC];
+  if (KVL) {
+    RowStage<KB, D, KVSTR> kst, vst;
+    kst.init(p.k_ss, tid);
+    vst.init(p.v_ss, tid);
+    kst.load((const bf16_t*)p.k + (int64_t)g * p.k_hs, p.k_ss, key0, lk);
+    vst.load((const bf16_t*)p.v + (int64_t)g * p.v_hs, p.v_ss, key0, lk);
+    kst.store(sKk);
+    vst.store(sVv);
+  } else {
     const bf16_t* Kp = (const bf16_t*)p.k + (int64_t)g * p.k_hs + mykey * p.k_ss + 8 * hi;
     const bf16_t* Vp = (const bf16_t*)p.v + (int64_t)g * p.v_hs + mykey * p.v_ss + 8 * hi;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < (KVL ? 1 : NC); ++c) {
       bf16x8 z = {};
       kreg[c] = key_ok ? *(const bf16x8*)(Kp + 16 * c) : z;
       vreg[c] = key_ok ? *(const bf16x8*)(Vp + 16 * c) : z;
     }
   }
+  const bf16_t* kop = sKk + (wave * 32 + l32) * KVSTR + 8 * hi;  // B operand rows (KVL)
+  const bf16_t* vop = sVv + (wave * 32 + l32) * KVSTR + 8 * hi;
   f32x16 dkacc[ND], dvacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
@@ -503,11 +538,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16 sacc = f32x16{}, pacc = f32x16{};
+        {
+          // operands of chunk c+1 are loaded while chunk c's MFMAs run
+          bf16x8 aq[2], ao[2], bk[2], bv[2];
+          auto ld = [&](int c, int slot) {
+            const int off = (qb * 32 + srow) * QSTR + 16 * c + 8 * hi;
+            aq[slot] = *(const bf16x8*)(sQ + off);
+            ao[slot] = *(const bf16x8*)(sdO + off);
+            bk[slot] = KVL ? *(const bf16x8*)(kop + 16 * c) : kreg[KVL ? 0 : c];
+            bv[slot] = KVL ? *(const bf16x8*)(vop + 16 * c) : vreg[KVL ? 0 : c];
+          };
+          ld(0, 0);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int off = (qb * 32 + srow) * QSTR + 16 * c + 8 * hi;
-          sacc = mfma32(*(const bf16x8*)(sQ + off), kreg[c], sacc);
-          pacc = mfma32(*(const bf16x8*)(sdO + off), vreg[c], pacc);
+          for (int c = 0; c < NC; ++c) {
+            if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
+            sacc = mfma32(aq[c & 1], bk[c & 1], sacc);
+            pacc = mfma32(ao[c & 1], bv[c & 1], pacc);
+          }
         }
         // register r is query q0 + qb*32 + 16*(r/8) + 8*hi + r%8
         bf16x8 pP[2], pS[2];
@@ -533,15 +580,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
           pP[hf] = p8;
           pS[hf] = s8;
         }
+        {
+          // (db, hf) step i+1's transposed operands load while step i's MFMAs run
+          bf16x8 ao[2], aq[2];
+          auto ld = [&](int i, int slot) {
+            const int db = i >> 1, cc = 2 * qb + (i & 1);
+            ao[slot] = rows_operand<QTT, QSTR, QTSTR>(sdO, sdOt, 16 * cc, 32 * db, lane);
+            aq[slot] = rows_operand<QTT, QSTR, QTSTR>(sQ, sQt, 16 * cc, 32 * db, lane);
+          };
+          ld(0, 0);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int cc = 2 * qb + hf;
-            const bf16x8 ao = rows_operand<QTT, QSTR, QTSTR>(sdO, sdOt, 16 * cc, 32 * db, lane);
-            dvacc[db] = mfma32(ao, pP[hf], dvacc[db]);
-            const bf16x8 aq = rows_operand<QTT, QSTR, QTSTR>(sQ, sQt, 16 * cc, 32 * db, lane);
-            dkacc[db] = mfma32(aq, pS[hf], dkacc[db]);
+          for (int i = 0; i < 2 * ND; ++i) {
+            if (i + 1 < 2 * ND) ld(i + 1, (i + 1) & 1);
+            const int db = i >> 1, hf = i & 1;
+            dvacc[db] = mfma32(ao[i & 1], pP[hf], dvacc[db]);
+            dkacc[db] = mfma32(aq[i & 1], pS[hf], dkacc[db]);
           }
         }
       }
@@ -608,8 +661,8 @@ hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   const int n_kt = (int)((p.km.len + 127) / 128);
   const int64_t grid = (int64_t)p.hkv * n_kt;
   if (grid > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, (bool)RA_BWD_QTT>), dim3((unsigned)grid), dim3(256), 0, s,
-                       p, n_kt);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, (bool)RA_BWD_QTT, (bool)RA_BWD_KVL>), dim3((unsigned)grid),
+                       dim3(256), 0, s, p, n_kt);
   return hipGetLastError();
 }
 

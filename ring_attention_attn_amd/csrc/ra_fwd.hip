@@ -220,12 +220,20 @@ __global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p
       const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
       // ---- S^T = K Q^T (rows of K in sigma order)
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      {
+        // chunk c+1's K operands load while chunk c's MFMAs run
+        bf16x8 a[2][2];
+        auto ld = [&](int c, int slot) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+          for (int kb = 0; kb < 2; ++kb)
+            a[slot][kb] = *(const bf16x8*)(sK + (kb * 32 + srow) * KSTR + 16 * c + 8 * hi);
+        };
+        ld(0, 0);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + srow) * KSTR + 16 * c + 8 * hi);
-          sacc[kb] = mfma32(a, qreg[c], sacc[kb]);
+        for (int c = 0; c < NC; ++c) {
+          if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(a[c & 1][kb], qreg[c], sacc[kb]);
         }
       }
       // register r of key block kb is key t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
@@ -272,22 +280,24 @@ __global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p
         for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
       }
       // ---- O^T += V^T P^T: lane half hi takes keys 16*cc + 8*hi .. +8
+      {
+        // step i = (db, cc); step i+1's V^T operand loads while step i's MFMA runs
+        auto ldv = [&](int i) {
+          const int db = i >> 2, cc = i & 3;
+          if (VT) return *(const bf16x8*)(sV + (32 * db + l32) * VSTR + 16 * cc + 8 * hi);
+          // rows 16cc + 8hi + {0..3} and {4..7}: the key order pk uses
+          const bf16_t* base = sV + (16 * cc + 8 * hi + (gi >> 2)) * VSTR + 32 * db + tr_col;
+          const bf16x4 lo4 = ds_read_tr(base);
+          const bf16x4 hi4 = ds_read_tr(base + 4 * VSTR);
+          return (bf16x8)__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 a[2];
+        a[0] = ldv(0);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          bf16x8 a;
-          if (VT) {
-            a = *(const bf16x8*)(sV + (32 * db + l32) * VSTR + 16 * cc + 8 * hi);
-          } else {
-            // keys 16cc + 4*(grp>>1) + e and +8: the order pk uses is
-            // {8hi + 0..7}; read rows 16cc + 8hi + {0..3, 4..7} instead
-            const bf16_t* base = sV + (16 * cc + 8 * hi + (gi >> 2)) * VSTR + 32 * db + tr_col;
-            const bf16x4 lo4 = ds_read_tr(base);
-            const bf16x4 hi4 = ds_read_tr(base + 4 * VSTR);
-            a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-          oacc[db] = mfma32(a, pk[cc >> 1][cc & 1], oacc[db]);
+        for (int i = 0; i < 4 * ND; ++i) {
+          if (i + 1 < 4 * ND) a[(i + 1) & 1] = ldv(i + 1);
+          const int db = i >> 2, cc = i & 3;
+          oacc[db] = mfma32(a[i & 1], pk[cc >> 1][cc & 1], oacc[db]);
         }
       }
     }
