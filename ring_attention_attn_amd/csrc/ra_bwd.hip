@@ -534,28 +534,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     if (!wave_skip) {
       const bool need_mask = (wkey0 + 32 > lk) || q0 + QT > lq || (p.causal && wk_hi > tq_lo);
       const TilePos tp(p.qm, q0, QT);
-      // one 32-query block at a time: S, dP -> P, dS -> dV^T, dK^T updates
+      // S and dP of both 32-query blocks are issued first; block 0's softmax
+      // then runs on the vector ALU while block 1's MFMAs execute, and block 1's
+      // softmax while block 0's dV/dK MFMAs execute
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-        {
-          // operands of chunk c+1 are loaded while chunk c's MFMAs run
-          bf16x8 aq[2], ao[2], bk[2], bv[2];
-          auto ld = [&](int c, int slot) {
-            const int off = (qb * 32 + srow) * QSTR + 16 * c + 8 * hi;
-            aq[slot] = *(const bf16x8*)(sQ + off);
-            ao[slot] = *(const bf16x8*)(sdO + off);
-            bk[slot] = KVL ? *(const bf16x8*)(kop + 16 * c) : kreg[KVL ? 0 : c];
-            bv[slot] = KVL ? *(const bf16x8*)(vop + 16 * c) : vreg[KVL ? 0 : c];
-          };
-          ld(0, 0);
+        sacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
+        // operands of chunk c+1 are loaded while chunk c's MFMAs run
+        bf16x8 aq[2], ao[2], bk[2], bv[2];
+        auto ld = [&](int c, int slot) {
+          const int off = (qb * 32 + srow) * QSTR + 16 * c + 8 * hi;
+          aq[slot] = *(const bf16x8*)(sQ + off);
+          ao[slot] = *(const bf16x8*)(sdO + off);
+          bk[slot] = KVL ? *(const bf16x8*)(kop + 16 * c) : kreg[KVL ? 0 : c];
+          bv[slot] = KVL ? *(const bf16x8*)(vop + 16 * c) : vreg[KVL ? 0 : c];
+        };
+        ld(0, 0);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
-            sacc = mfma32(aq[c & 1], bk[c & 1], sacc);
-            pacc = mfma32(ao[c & 1], bv[c & 1], pacc);
-          }
+        for (int c = 0; c < NC; ++c) {
+          if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
+          sacc[qb] = mfma32(aq[c & 1], bk[c & 1], sacc[qb]);
+          pacc[qb] = mfma32(ao[c & 1], bv[c & 1], pacc[qb]);
         }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
         // register r is query q0 + qb*32 + 16*(r/8) + 8*hi + r%8
         bf16x8 pP[2], pS[2];
 #pragma unroll
@@ -569,33 +574,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
             const int r = 8 * hf + e;
             const float l2 = e < 4 ? la[e] : lb[e - 4];
             const float dl = e < 4 ? da[e] : db_[e - 4];
-            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -l2));
+            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], p.scale_log2, -l2));
             if (need_mask) {
               const bool vis = (qo + e < tp.nvalid) & (tp.pos(qo + e) >= kmin);
               pr = vis ? pr : 0.f;
             }
             p8[e] = (bf16_t)pr;
-            s8[e] = (bf16_t)(pr * (pacc[r] - dl));
+            s8[e] = (bf16_t)(pr * (pacc[qb][r] - dl));
           }
           pP[hf] = p8;
           pS[hf] = s8;
         }
-        {
-          // (db, hf) step i+1's transposed operands load while step i's MFMAs run
-          bf16x8 ao[2], aq[2];
-          auto ld = [&](int i, int slot) {
-            const int db = i >> 1, cc = 2 * qb + (i & 1);
-            ao[slot] = rows_operand<QTT, QSTR, QTSTR>(sdO, sdOt, 16 * cc, 32 * db, lane);
-            aq[slot] = rows_operand<QTT, QSTR, QTSTR>(sQ, sQt, 16 * cc, 32 * db, lane);
-          };
-          ld(0, 0);
+        // (db, hf) step i+1's transposed operands load while step i's MFMAs run
+        bf16x8 ao[2], aq[2];
+        auto ld = [&](int i, int slot) {
+          const int db = i >> 1, cc = 2 * qb + (i & 1);
+          ao[slot] = rows_operand<QTT, QSTR, QTSTR>(sdO, sdOt, 16 * cc, 32 * db, lane);
+          aq[slot] = rows_operand<QTT, QSTR, QTSTR>(sQ, sQt, 16 * cc, 32 * db, lane);
+        };
+        ld(0, 0);
 #pragma unroll
-          for (int i = 0; i < 2 * ND; ++i) {
-            if (i + 1 < 2 * ND) ld(i + 1, (i + 1) & 1);
-            const int db = i >> 1, hf = i & 1;
-            dvacc[db] = mfma32(ao[i & 1], pP[hf], dvacc[db]);
-            dkacc[db] = mfma32(aq[i & 1], pS[hf], dkacc[db]);
-          }
+        for (int i = 0; i < 2 * ND; ++i) {
+          if (i + 1 < 2 * ND) ld(i + 1, (i + 1) & 1);
+          const int db = i >> 1, hf = i & 1;
+          dvacc[db] = mfma32(ao[i & 1], pP[hf], dvacc[db]);
+          dkacc[db] = mfma32(aq[i & 1], pS[hf], dkacc[db]);
         }
       }
     }
