@@ -4,33 +4,31 @@
 // LoongTrain", "The Communication Overhead and Causal Imbalance of Ring
 // Attention"; scale 1/sqrt(d) and softmax(QK^T scale) V as in its "Step 3").
 //
-// bf16 path (gfx950 MFMA): a workgroup of 4 waves shares one KV head; two
-// workgroups share a CU (two waves per SIMD). Each wave owns 32 query rows of
-// one query head; the waves of a workgroup are the grouped query heads that
-// read the same K/V (GQA packing) and/or consecutive row blocks. Per 64-key
-// tile, K is staged in LDS row-major and V transposed (V^T[d][key], built by
-// register shuffles). Each wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 so that a lane owns one query column: the online
-// softmax row max/sum are in-lane plus one exchange with the other half-wave.
-// K rows are fed in the sigma order (ra_tile.h), so each 8-register chunk of
-// exp2(S^T - m) covers 8 consecutive keys and, rounded to bf16, is directly the
-// B operand of O^T += V^T P^T, whose A operand is one 16-byte LDS read of V^T.
+// bf16 path (gfx950 MFMA): a workgroup of 8 waves (two per SIMD) shares one KV
+// head. Each wave owns 32 query rows of one query head; the waves of a
+// workgroup are the grouped query heads that read the same K/V (GQA packing)
+// and/or consecutive row blocks. K/V tiles of 64 keys are copied global -> LDS
+// by DMA. Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that
+// a lane owns one query column: the online softmax row max/sum are in-lane plus
+// one exchange with the other half-wave (v_permlane32_swap). K rows are fed in
+// the sigma order (ra_tile.h), so each 8-register chunk of exp2(S^T - m) covers
+// 8 consecutive keys and, rounded to bf16, is directly the B operand of
+// O^T += V^T P^T, whose A operand is read transposed from row-major V.
 // Tiles whose keys are all later than the workgroup's queries are skipped;
-// fully visible tiles run without masking; O is rescaled only when a row max
-// moved.
+// fully visible tiles run a mask-free copy of the tile code. The exponent shift
+// (running max) moves only when a row's tile max exceeds it by 2^8, so O is
+// rarely rescaled; the result is the same softmax, since LSE and the
+// normalisation use the same shift.
 //
 // fp32 path: a plain VALU kernel (one or two lanes per query row), used for the
 // fp32 workload and kept deliberately simple.
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "ra_internal.h"
 #include "ra_tile.h"
-
-// minimum resident workgroups per CU (2: two waves per SIMD hide latency)
-#ifndef RA_FWD_MINB
-#define RA_FWD_MINB 2
-#endif
 
 namespace {
 
@@ -109,20 +107,28 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 }
 
 // ============================================================= MFMA kernel
-// VT selects how V^T reaches the O^T += V^T P^T product: true = V staged
-// transposed in LDS (register transpose, one 16-byte read per operand),
-// false = V staged row-major and read with ds_read_b64_tr_b16.
-template <int D, bool VT>
-__global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
-                                                                    int rows_per_wg) {
-  constexpr int KT = 64;          // keys per LDS tile
-  constexpr int KSTR = D + 8;     // sK row stride (elements)
-  constexpr int VSTR = VT ? KT + 8 : D + 16;  // V^T rows are d (VT) or V rows are keys
-  constexpr int VROWS = VT ? D : KT;
-  constexpr int NC = D / 16;      // 16-wide d chunks (QK^T contraction steps)
-  constexpr int ND = D / 32;      // 32-wide d blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[VROWS * VSTR];
+// A workgroup is 8 waves (two per SIMD); wave w owns 32 query rows of one query
+// head. K and V tiles of 64 keys reach LDS by DMA (double-buffered, one barrier
+// per tile); each wave runs 16 MFMAs for S^T and 16 for O^T per tile. K rows
+// are read with 16-byte loads (row stride 17 chunks: conflict-free), V^T
+// operands with ds_read_b64_tr_b16 (row stride 20 chunks: conflict-free). The
+// tile body is instantiated unmasked (straight-line code) and masked
+// (diagonal tiles, ragged tails).
+template <int D>
+__global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
+                                                          int rows_per_wg) {
+  constexpr int NW = 8;            // waves per workgroup
+  constexpr int KT = 64;           // keys per LDS tile
+  constexpr int KSTR = D + 8;      // sK row stride (elements): odd number of 16-byte chunks
+  constexpr int VSTR = D == 128 ? D + 32 : D + 32;  // sV row stride: 20 (D=128) / 12 (D=64) chunks
+  constexpr int NC = D / 16;       // 16-wide d chunks (QK^T contraction steps)
+  constexpr int ND = D / 32;       // 32-wide d blocks of O^T
+  // log2-domain headroom before the running max is moved: P stays <= 2^8
+  constexpr float kThresh = 8.f;
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[KT * KSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[KT * KSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[KT * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[KT * VSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,6 +157,17 @@ __global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p
   const bf16_t* K = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
   const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
 
+  // stale LDS must hold finite values: keys past the end are never read into
+  // P != 0, but 0 * NaN would poison O
+  for (int i = tid; i < KT * KSTR / 8; i += NW * 64) {
+    ((bf16x8*)sK0)[i] = bf16x8{};
+    ((bf16x8*)sK1)[i] = bf16x8{};
+  }
+  for (int i = tid; i < KT * VSTR / 8; i += NW * 64) {
+    ((bf16x8*)sV0)[i] = bf16x8{};
+    ((bf16x8*)sV1)[i] = bf16x8{};
+  }
+
   // Q^T as the B operand: lane holds query column l32, d = 16c + 8*hi .. +8
   bf16x8 qreg[NC];
   const int64_t qrow = row0 + l32;
@@ -169,7 +186,7 @@ __global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p
   f32x16 oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max, scaled (log2) units
+  float m_run = -INFINITY;  // running max (log2 units) used as the exponent shift
   float l_run = 0.f;        // running sum of this half-wave's keys
 
   const int n_kt = (int)((lk + KT - 1) / KT);
@@ -188,125 +205,134 @@ __global__ __launch_bounds__(256, RA_FWD_MINB) void fwd_mfma_kernel(StepParams p
     return t;
   };
 
-  // lane roles of the transposing read (VT == false)
-  const int grp = lane >> 4, gi = lane & 15;
-  const int tr_col = 16 * (grp & 1) + 4 * (gi & 3);
-
-  RowStage<KT, D, KSTR> ks;
-  ks.init(p.k_ss, tid);
-  RowStage<KT, D, VSTR> vs_rows;
-  ColStage<KT, D, VSTR> vs_cols;
-  if (VT) vs_cols.init(p.v_ss, tid); else vs_rows.init(p.v_ss, tid);
-  auto load_tile = [&](int t) {
-    ks.load(K, p.k_ss, (int64_t)t * KT, lk);
-    if (VT) vs_cols.load(V, p.v_ss, (int64_t)t * KT, lk);
-    else vs_rows.load(V, p.v_ss, (int64_t)t * KT, lk);
+  DmaStage<KT, D, KSTR * 2, NW> kst;
+  DmaStage<KT, D, VSTR * 2, NW> vst;
+  kst.init(p.k_ss, wave, lane);
+  vst.init(p.v_ss, wave, lane);
+  auto stage = [&](int t, auto bsel) {
+    constexpr int B = decltype(bsel)::value;
+    kst.issue(K, p.k_ss, (int64_t)t * KT, lk, B ? sK1 : sK0);
+    vst.issue(V, p.v_ss, (int64_t)t * KT, lk, B ? sV1 : sV0);
   };
 
-  int t = next_visible(0);
-  if (t < n_kt) load_tile(t);
-  while (t < n_kt) {
-    __syncthreads();
-    ks.store(sK);
-    if (VT) vs_cols.store(sV); else vs_rows.store(sV);
-    __syncthreads();
-    const int tn = next_visible(t + 1);
-    if (tn < n_kt) load_tile(tn);
+  // per-lane LDS offsets (elements); everything else is an immediate offset
+  const int k_lane = srow * KSTR + 8 * hi;
+  const int grp = lane >> 4, gi = lane & 15;
+  const int v_lane = (8 * hi + (gi >> 2)) * VSTR + 16 * (grp & 1) + 4 * (gi & 3);
 
+  // ---- one 64-key tile: S^T = K Q^T, online softmax (exp2 domain), O^T += V^T P^T
+  auto body = [&](int t, auto bsel, bool need_mask) {
+    constexpr int B = decltype(bsel)::value;
+    const bf16_t* cK = (B ? sK1 : sK0) + k_lane;
+    const bf16_t* cV = (B ? sV1 : sV0) + v_lane;
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = mfma32(*(const bf16x8*)(cK + kb * 32 * KSTR + 16 * c), qreg[c], sacc[kb]);
+    // register r of key block kb is key t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
+    if (need_mask) {  // wave-uniform: one branch around branch-free code
+      // the lane part (8*hi) of each key offset is folded into the per-tile
+      // bounds so each register compares against a constant
+      const TileRows tk(p.km, (int64_t)t * KT, KT);
+      const MaskBounds mb(tk, qlim, 8 * hi, p.causal);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool vis = mb.key_visible(kb * 32 + 16 * (r >> 3) + (r & 7));
+          sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+        }
+    }
+    // ---- tile row max on raw scores (scale > 0), over both lane halves
+    float mx = fmax3(sacc[0][0], sacc[0][1], sacc[0][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mx = fmax3(mx, sacc[0][r], sacc[0][r + 1]);
+    mx = fmax3(mx, sacc[0][15], sacc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 15; r += 2) mx = fmax3(mx, sacc[1][r], sacc[1][r + 1]);
+    mx = __builtin_fmaxf(mx, sacc[1][15]);
+    mx = max_halves(mx);
+    const float mt = mx * p.scale_log2;
+    // the shift moves only when a row's max outgrows it by kThresh (rarely after
+    // the first tiles); P = exp2(s - m_run) <= 2^kThresh otherwise
+    if (__any(mt > m_run + kThresh)) {
+      const float m_new = __builtin_fmaxf(m_run, mt);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pk[2][2];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * hf + e], p.scale_log2, -m_use));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          rs0 += pe[e];
+          rs1 += pe[e + 1];
+        }
+        pk[kb][hf] = pack_bf16x8(pe);
+      }
+    l_run += rs0 + rs1;
+    // ---- O^T += V^T P^T: V^T operand = keys 16*cc + 8*hi .. +8 of d row
+    // 32*db + l32, read transposed from row-major V; consecutive MFMAs use
+    // different accumulators
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16_t* a = cV + 16 * cc * VSTR + 32 * db;
+        const bf16x4 lo4 = ds_read_tr(a);
+        const bf16x4 hi4 = ds_read_tr(a + 4 * VSTR);
+        const bf16x8 av = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = mfma32(av, pk[cc >> 1][cc & 1], oacc[db]);
+      }
+  };
+
+  auto compute = [&](int t, auto bsel) {
     int64_t klo, khi;
     tile_bounds(t, klo, khi);
     const bool wave_skip = !wave_active || (p.causal && klo > wq_hi);
-    if (!wave_skip) {
-      const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
-      // ---- S^T = K Q^T (rows of K in sigma order)
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      {
-        // chunk c+1's K operands load while chunk c's MFMAs run
-        bf16x8 a[2][2];
-        auto ld = [&](int c, int slot) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            a[slot][kb] = *(const bf16x8*)(sK + (kb * 32 + srow) * KSTR + 16 * c + 8 * hi);
-        };
-        ld(0, 0);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(a[c & 1][kb], qreg[c], sacc[kb]);
-        }
-      }
-      // register r of key block kb is key t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
-      if (need_mask) {
-        const TilePos tp(p.km, (int64_t)t * KT, KT);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-            const bool vis = (off < tp.nvalid) & (tp.pos(off) <= qlim);
-            sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
-          }
-      }
-      // ---- online softmax in the exp2 domain; max taken on raw scores (scale > 0)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * p.scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      bf16x8 pk[2][2];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          bf16x8 v8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * hf + e], p.scale_log2, -m_use));
-            rs += pe;
-            v8[e] = (bf16_t)pe;
-          }
-          pk[kb][hf] = v8;
-        }
-      l_run = l_run * alpha + rs;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-      }
-      // ---- O^T += V^T P^T: lane half hi takes keys 16*cc + 8*hi .. +8
-      {
-        // step i = (db, cc); step i+1's V^T operand loads while step i's MFMA runs
-        auto ldv = [&](int i) {
-          const int db = i >> 2, cc = i & 3;
-          if (VT) return *(const bf16x8*)(sV + (32 * db + l32) * VSTR + 16 * cc + 8 * hi);
-          // rows 16cc + 8hi + {0..3} and {4..7}: the key order pk uses
-          const bf16_t* base = sV + (16 * cc + 8 * hi + (gi >> 2)) * VSTR + 32 * db + tr_col;
-          const bf16x4 lo4 = ds_read_tr(base);
-          const bf16x4 hi4 = ds_read_tr(base + 4 * VSTR);
-          return (bf16x8)__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        bf16x8 a[2];
-        a[0] = ldv(0);
-#pragma unroll
-        for (int i = 0; i < 4 * ND; ++i) {
-          if (i + 1 < 4 * ND) a[(i + 1) & 1] = ldv(i + 1);
-          const int db = i >> 2, cc = i & 3;
-          oacc[db] = mfma32(a[i & 1], pk[cc >> 1][cc & 1], oacc[db]);
-        }
-      }
-    }
+    if (wave_skip) return;
+    const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
+    body(t, bsel, need_mask);
+  };
+
+  __syncthreads();  // zero-fill done before any DMA lands
+  int t = next_visible(0);
+  if (t < n_kt) stage(t, std::integral_constant<int, 0>{});
+  // tiles alternate between the two buffers; the loop is unrolled by two so
+  // that each buffer is a distinct array (the compiler then knows the DMA into
+  // one buffer does not alias the reads of the other)
+  while (t < n_kt) {
+    wait_vmem();
+    __syncthreads();  // tile t visible in buffer 0; every wave is done with buffer 1
+    int tn = next_visible(t + 1);
+    if (tn < n_kt) stage(tn, std::integral_constant<int, 1>{});
+    compute(t, std::integral_constant<int, 0>{});
+    t = tn;
+    if (t >= n_kt) break;
+    wait_vmem();
+    __syncthreads();
+    tn = next_visible(t + 1);
+    if (tn < n_kt) stage(tn, std::integral_constant<int, 0>{});
+    compute(t, std::integral_constant<int, 1>{});
     t = tn;
   }
 
   // ---- epilogue: normalise, write O_step [row][h][d] and LSE_step [h][row]
   if (!wave_active) return;
-  const float ltot = l_run + __shfl_xor(l_run, 32);
+  const float ltot = sum_halves(l_run);
   if (qok) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     float* orow = p.o + qrow * p.o_ss + (int64_t)h * p.o_hs;
@@ -333,20 +359,15 @@ int gcd_int(int a, int b) {
   return a;
 }
 
-#ifndef RA_FWD_VT
-#define RA_FWD_VT 1
-#endif
-
 template <int D>
 hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
-  const int hpw = gcd_int(p.group, 4);
-  const int rb = 4 / hpw;
-  const int rows_per_wg = rb * 32;
+  const int hpw = gcd_int(p.group, 4);  // query heads per row block (GQA packing)
+  const int rows_per_wg = (8 / hpw) * 32;
   const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
   const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, (bool)RA_FWD_VT>), dim3((unsigned)grid), dim3(256), 0, s, p,
-                     hpw, n_qt, rows_per_wg);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw, n_qt,
+                     rows_per_wg);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@
 // product that contracts over those rows, with the other operand read from a
 // transposed LDS tile by one 16-byte load.
 #pragma once
+#include <limits.h>
 #include "ra_internal.h"
 
 __device__ __forceinline__ int sigma32(int l32) {
@@ -29,6 +30,34 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int half) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (bf16_t)x[8 * half + e];
   return r;
+}
+
+// Eight floats rounded to bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16_t)x[e];
+  return r;
+}
+
+// max of three floats in one instruction (v_max3_f32); inputs are never NaN
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// Reductions over the two halves of a wave (lanes l and l ^ 32) with
+// v_permlane32_swap instead of an LDS permute: with both operands = x, the
+// swap leaves x[l % 32] in the first result and x[l % 32 + 32] in the second,
+// so every lane combines the same two values in the same order.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Transpose a 4-row x 8-column bf16 block held as four 8-wide rows into eight
@@ -130,6 +159,51 @@ struct ColStage {
   }
 };
 
+// ---- global -> LDS staging by LDS-DMA buffer loads (no registers, no ds_write).
+// The tile's T rows of D bf16 are laid out in LDS with a row stride of RSB
+// bytes (padding chosen per use for conflict-free reads). Instruction j of the
+// workgroup fills LDS bytes [1024 j, 1024 j + 1024): lane i writes the 16 bytes
+// at p = 1024 j + 16 i, i.e. chunk (p % RSB) / 16 of tile row p / RSB; a lane
+// that lands in a row's padding loads that row's first chunk (harmless). Rows
+// past the descriptor's range read as zero.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int T, int D, int RSB, int NW>
+struct DmaStage {
+  static constexpr int NJ = T * RSB / 1024;
+  static constexpr int PER = (NJ + NW - 1) / NW;
+  static_assert(T * RSB % 1024 == 0 && RSB % 16 == 0 && RSB >= 2 * D, "whole 1 KiB blocks");
+  uint32_t voff[PER];
+  int wave;
+  __device__ __forceinline__ void init(int64_t ss, int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int p = 1024 * (wave + k * NW) + 16 * lane;
+      const int row = p / RSB;
+      int ch = (p % RSB) / 16;
+      ch = ch < D / 8 ? ch : 0;
+      voff[k] = (uint32_t)(((int64_t)(row < T ? row : 0) * ss + 8 * ch) * 2);
+    }
+  }
+  // tile rows [row0, row0 + T) of `base` (row stride ss elements) into `lds`
+  __device__ __forceinline__ void issue(const bf16_t* base, int64_t ss, int64_t row0,
+                                        int64_t nrows, bf16_t* lds) const {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = wave + k * NW;
+      if (j < NJ)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((char*)lds + 1024 * j), 16,
+                                                 voff[k], 0, 0, 0);
+    }
+  }
+};
+
+// Wait until this wave's outstanding vector-memory operations (LDS-DMA loads
+// included) are complete.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i of
@@ -157,6 +231,45 @@ struct TilePos {
   }
   __device__ __forceinline__ int pos(int off) const {
     return one_seg ? base + off : (int)seg_pos(*m, t0 + off);
+  }
+};
+
+// int32 positions of the rows [t0, t0 + n) of a SegMap, for branch-free
+// masking: row t0 + off is at pos(off) while off < split (first run), and
+// rows at or past nvalid do not exist. All fields are wave-uniform.
+struct TileRows {
+  int base0, base1, split, nvalid;
+  __device__ __forceinline__ TileRows(const SegMap& m, int64_t t0, int n) {
+    base0 = (int)(m.pos0 + t0);
+    base1 = (int)(m.pos1 + t0 - m.seg_len);
+    const int64_t s = m.seg_len - t0;
+    split = s < 0 ? 0 : (s > n ? n : (int)s);
+    const int64_t v = m.len - t0;
+    nvalid = v < 0 ? 0 : (v > n ? n : (int)v);
+  }
+  __device__ __forceinline__ int pos(int off) const { return (off < split ? base0 : base1) + off; }
+};
+
+// Visibility of the keys of a tile to one query of position qlim (the lane's
+// query), for key offsets c + u where u is the lane's part of the offset and
+// c a compile-time constant: c + u must exist (< nvalid) and, when causal, sit
+// at a position <= qlim.
+struct MaskBounds {
+  int nv, sp, a0, a1;
+  __device__ __forceinline__ MaskBounds(const TileRows& t, int qlim, int u, int causal) {
+    nv = t.nvalid - u;
+    sp = t.split - u;
+    if (causal) {
+      // qlim - base - u, saturated to the int32 range
+      const int64_t x0 = (int64_t)qlim - t.base0 - u, x1 = (int64_t)qlim - t.base1 - u;
+      a0 = x0 > INT_MAX ? INT_MAX : (x0 < INT_MIN ? INT_MIN : (int)x0);
+      a1 = x1 > INT_MAX ? INT_MAX : (x1 < INT_MIN ? INT_MIN : (int)x1);
+    } else {
+      a0 = a1 = INT_MAX;
+    }
+  }
+  __device__ __forceinline__ bool key_visible(int c) const {
+    return (c < nv) & (c <= (c < sp ? a0 : a1));
   }
 };
 
