@@ -30,6 +30,11 @@
 #include "ra_internal.h"
 #include "ra_tile.h"
 
+// explicit MFMA / vector instruction interleaving of the pipelined tile step
+#ifndef RA_FWD_SCHED
+#define RA_FWD_SCHED 1
+#endif
+
 namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -108,27 +113,31 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 
 // ============================================================= MFMA kernel
 // A workgroup is 8 waves (two per SIMD); wave w owns 32 query rows of one query
-// head. K and V tiles of 64 keys reach LDS by DMA (double-buffered, one barrier
-// per tile); each wave runs 16 MFMAs for S^T and 16 for O^T per tile. K rows
-// are read with 16-byte loads (row stride 17 chunks: conflict-free), V^T
-// operands with ds_read_b64_tr_b16 (row stride 20 chunks: conflict-free). The
-// tile body is instantiated unmasked (straight-line code) and masked
-// (diagonal tiles, ragged tails).
+// head. K and V tiles of 64 keys reach LDS by DMA into three rotating buffers
+// (one barrier per tile). The loop is software-pipelined: while the softmax and
+// O^T += V^T P^T of tile t run, the 16 MFMAs of S^T for the next tile are
+// issued in the same basic block, so vector and matrix work overlap inside
+// each wave. K rows are read with 16-byte loads (row stride of an odd number
+// of 16-byte chunks: conflict-free), V^T operands with ds_read_b64_tr_b16 (row
+// stride 20 (D = 128) or 12 (D = 64) chunks: conflict-free). Diagonal tiles
+// and ragged tails add one branch-free masking block.
 template <int D>
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
                                                           int rows_per_wg) {
   constexpr int NW = 8;            // waves per workgroup
   constexpr int KT = 64;           // keys per LDS tile
   constexpr int KSTR = D + 8;      // sK row stride (elements): odd number of 16-byte chunks
-  constexpr int VSTR = D == 128 ? D + 32 : D + 32;  // sV row stride: 20 (D=128) / 12 (D=64) chunks
+  constexpr int VSTR = D + 32;     // sV row stride: 20 (D=128) / 12 (D=64) chunks
   constexpr int NC = D / 16;       // 16-wide d chunks (QK^T contraction steps)
   constexpr int ND = D / 32;       // 32-wide d blocks of O^T
   // log2-domain headroom before the running max is moved: P stays <= 2^8
   constexpr float kThresh = 8.f;
   __shared__ __attribute__((aligned(1024))) bf16_t sK0[KT * KSTR];
   __shared__ __attribute__((aligned(1024))) bf16_t sK1[KT * KSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK2[KT * KSTR];
   __shared__ __attribute__((aligned(1024))) bf16_t sV0[KT * VSTR];
   __shared__ __attribute__((aligned(1024))) bf16_t sV1[KT * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV2[KT * VSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,10 +171,12 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   for (int i = tid; i < KT * KSTR / 8; i += NW * 64) {
     ((bf16x8*)sK0)[i] = bf16x8{};
     ((bf16x8*)sK1)[i] = bf16x8{};
+    ((bf16x8*)sK2)[i] = bf16x8{};
   }
   for (int i = tid; i < KT * VSTR / 8; i += NW * 64) {
     ((bf16x8*)sV0)[i] = bf16x8{};
     ((bf16x8*)sV1)[i] = bf16x8{};
+    ((bf16x8*)sV2)[i] = bf16x8{};
   }
 
   // Q^T as the B operand: lane holds query column l32, d = 16c + 8*hi .. +8
@@ -189,30 +200,27 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   float m_run = -INFINITY;  // running max (log2 units) used as the exponent shift
   float l_run = 0.f;        // running sum of this half-wave's keys
 
-  const int n_kt = (int)((lk + KT - 1) / KT);
-  auto tile_bounds = [&](int t, int64_t& lo, int64_t& hi_) {
-    const int64_t k0 = (int64_t)t * KT;
-    seg_bounds(p.km, k0, k0 + KT < lk ? k0 + KT : lk, lo, hi_);
-  };
-  auto next_visible = [&](int t) {
-    while (t < n_kt) {
-      if (!p.causal) return t;
-      int64_t lo, hh;
-      tile_bounds(t, lo, hh);
-      if (lo <= gq_hi) return t;
-      ++t;
-    }
-    return t;
-  };
+  // visible key tiles of the workgroup, and the tiles this wave must mask
+  const KeyTiles<KT> kt_wg(p.km, p.causal, gq_lo, gq_hi);
+  const KeyTiles<KT> kt_w(p.km, p.causal, wq_lo, wq_hi);
+  const int n_kt = kt_wg.n;
+  auto next_visible = [&](int t) { return kt_wg.next(t); };
 
   DmaStage<KT, D, KSTR * 2, NW> kst;
   DmaStage<KT, D, VSTR * 2, NW> vst;
   kst.init(p.k_ss, wave, lane);
   vst.init(p.v_ss, wave, lane);
-  auto stage = [&](int t, auto bsel) {
-    constexpr int B = decltype(bsel)::value;
-    kst.issue(K, p.k_ss, (int64_t)t * KT, lk, B ? sK1 : sK0);
-    vst.issue(V, p.v_ss, (int64_t)t * KT, lk, B ? sV1 : sV0);
+  auto kbuf = [&](auto b) -> bf16_t* {
+    constexpr int B = decltype(b)::value;
+    return B == 0 ? sK0 : (B == 1 ? sK1 : sK2);
+  };
+  auto vbuf = [&](auto b) -> bf16_t* {
+    constexpr int B = decltype(b)::value;
+    return B == 0 ? sV0 : (B == 1 ? sV1 : sV2);
+  };
+  auto stage = [&](int t, auto b) {
+    kst.issue(K, p.k_ss, (int64_t)t * KT, lk, kbuf(b));
+    vst.issue(V, p.v_ss, (int64_t)t * KT, lk, vbuf(b));
   };
 
   // per-lane LDS offsets (elements); everything else is an immediate offset
@@ -220,19 +228,22 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   const int grp = lane >> 4, gi = lane & 15;
   const int v_lane = (8 * hi + (gi >> 2)) * VSTR + 16 * (grp & 1) + 4 * (gi & 3);
 
-  // ---- one 64-key tile: S^T = K Q^T, online softmax (exp2 domain), O^T += V^T P^T
-  auto body = [&](int t, auto bsel, bool need_mask) {
-    constexpr int B = decltype(bsel)::value;
-    const bf16_t* cK = (B ? sK1 : sK0) + k_lane;
-    const bf16_t* cV = (B ? sV1 : sV0) + v_lane;
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T of the tile in buffer b; register r of key block kb is key
+  // t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
+  auto scores = [&](auto b, f32x16 (&sacc)[2]) {
+    const bf16_t* cK = kbuf(b) + k_lane;
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = mfma32(*(const bf16x8*)(cK + kb * 32 * KSTR + 16 * c), qreg[c], sacc[kb]);
-    // register r of key block kb is key t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
-    if (need_mask) {  // wave-uniform: one branch around branch-free code
+  };
+  // mask scores of tile t for this wave's queries (keys past the end, and
+  // causally later keys) and move the exponent shift if the tile needs it
+  auto prepare = [&](int t, f32x16 (&sacc)[2]) {
+    if (!wave_active || !kt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
       // the lane part (8*hi) of each key offset is folded into the per-tile
       // bounds so each register compares against a constant
       const TileRows tk(p.km, (int64_t)t * KT, KT);
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
           sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
         }
     }
-    // ---- tile row max on raw scores (scale > 0), over both lane halves
+    // tile row max on raw scores (scale > 0), over both lane halves
     float mx = fmax3(sacc[0][0], sacc[0][1], sacc[0][2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) mx = fmax3(mx, sacc[0][r], sacc[0][r + 1]);
@@ -265,6 +276,11 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
 #pragma unroll
       for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
     }
+  };
+  // P = exp2(S^T scale_log2 - m_run) in bf16, and O^T += V^T P^T from buffer b:
+  // the V^T operand is keys 16*cc + 8*hi .. +8 of d row 32*db + l32, read
+  // transposed from row-major V; consecutive MFMAs use different accumulators
+  auto accumulate = [&](auto b, const f32x16 (&sacc)[2]) {
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pk[2][2];
     float rs0 = 0.f, rs1 = 0.f;
@@ -284,9 +300,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
         pk[kb][hf] = pack_bf16x8(pe);
       }
     l_run += rs0 + rs1;
-    // ---- O^T += V^T P^T: V^T operand = keys 16*cc + 8*hi .. +8 of d row
-    // 32*db + l32, read transposed from row-major V; consecutive MFMAs use
-    // different accumulators
+    const bf16_t* cV = vbuf(b) + v_lane;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -299,35 +313,74 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
       }
   };
 
-  auto compute = [&](int t, auto bsel) {
-    int64_t klo, khi;
-    tile_bounds(t, klo, khi);
-    const bool wave_skip = !wave_active || (p.causal && klo > wq_hi);
-    if (wave_skip) return;
-    const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
-    body(t, bsel, need_mask);
+  // Issue order of the step's block: LDS reads run about six MFMAs ahead of
+  // their use; each of the 16 score MFMAs sits between four softmax vector
+  // instructions, each of the 16 O^T MFMAs between three.
+  auto interleave = [&]() {
+#if RA_FWD_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads: K for scores 0-5
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#endif
+  };
+
+  // One pipeline step. On entry sc holds the prepared scores of tile t (buffer
+  // bc) and the DMA of tile tn (buffer bn) is in flight. The barrier makes tn
+  // visible and frees bn2 (last read one step ago) for the DMA of the tile after
+  // tn. Scores of tn are computed (unconditionally: past the end they are
+  // discarded) in the same block as tile t's softmax and O update.
+  f32x16 sc[2], sn[2];
+  int t = next_visible(0), tn = n_kt;
+  auto step = [&](auto bc, auto bn, auto bn2) {
+    wait_vmem();
+    __syncthreads();
+    const int tn2 = tn < n_kt ? next_visible(tn + 1) : n_kt;
+    if (tn2 < n_kt) stage(tn2, bn2);
+    scores(bn, sn);
+    accumulate(bc, sc);
+    interleave();
+    t = tn;
+    tn = tn2;
+    if (t < n_kt) {
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+      prepare(t, sc);
+    }
+    return t < n_kt;
   };
 
   __syncthreads();  // zero-fill done before any DMA lands
-  int t = next_visible(0);
-  if (t < n_kt) stage(t, std::integral_constant<int, 0>{});
-  // tiles alternate between the two buffers; the loop is unrolled by two so
-  // that each buffer is a distinct array (the compiler then knows the DMA into
-  // one buffer does not alias the reads of the other)
-  while (t < n_kt) {
-    wait_vmem();
-    __syncthreads();  // tile t visible in buffer 0; every wave is done with buffer 1
-    int tn = next_visible(t + 1);
-    if (tn < n_kt) stage(tn, std::integral_constant<int, 1>{});
-    compute(t, std::integral_constant<int, 0>{});
-    t = tn;
-    if (t >= n_kt) break;
+  if (t < n_kt) {
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+    stage(t, B0{});
+    tn = next_visible(t + 1);
+    if (tn < n_kt) stage(tn, B1{});
     wait_vmem();
     __syncthreads();
-    tn = next_visible(t + 1);
-    if (tn < n_kt) stage(tn, std::integral_constant<int, 0>{});
-    compute(t, std::integral_constant<int, 1>{});
-    t = tn;
+    scores(B0{}, sc);
+    prepare(t, sc);
+    // buffers rotate 0 -> 1 -> 2; unrolled so each buffer is a distinct array
+    // (the compiler then knows a DMA into one does not alias reads of another)
+    while (step(B0{}, B1{}, B2{}) && step(B1{}, B2{}, B0{}) && step(B2{}, B0{}, B1{})) {
+    }
   }
 
   // ---- epilogue: normalise, write O_step [row][h][d] and LSE_step [h][row]

@@ -250,6 +250,57 @@ struct TileRows {
   __device__ __forceinline__ int pos(int off) const { return (off < split ? base0 : base1) + off; }
 };
 
+// Rows of a SegMap whose position is <= x: [0, c0) of the first run and
+// [seg_len, seg_len + c1) of the second (positions increase along each run).
+// int32 results: lengths and positions fit in int32 (checked on the host).
+__device__ __forceinline__ void rows_upto(const SegMap& m, int64_t x, int& c0, int& c1) {
+  const int64_t a = x - m.pos0 + 1, b = x - m.pos1 + 1, n1 = m.len - m.seg_len;
+  c0 = (int)(a < 0 ? 0 : (a > m.seg_len ? m.seg_len : a));
+  c1 = (int)(b < 0 ? 0 : (b > n1 ? n1 : b));
+}
+
+// Key tiles of TK rows of a KV chunk as seen by a block of queries, in int32:
+// tiles holding a key at or before the block's last query position
+// (visible: [0, a1) and [b0, b1)), and whether a tile is free of keys after
+// the block's first query position and of rows past the end (mask-free).
+template <int TK>
+struct KeyTiles {
+  int n, len, seg, a1, b0, b1, e0, e1;
+  __device__ __forceinline__ KeyTiles(const SegMap& km, int causal, int64_t q_first,
+                                      int64_t q_last) {
+    len = (int)km.len;
+    seg = (int)km.seg_len;
+    n = (len + TK - 1) / TK;
+    if (causal) {
+      int c0, c1;
+      rows_upto(km, q_last, c0, c1);
+      a1 = (c0 + TK - 1) / TK;
+      b0 = seg / TK;
+      b1 = c1 > 0 ? (seg + c1 + TK - 1) / TK : b0;
+      rows_upto(km, q_first, e0, e1);
+    } else {
+      a1 = n;
+      b0 = b1 = 0;
+      e0 = seg;
+      e1 = len - seg;
+    }
+  }
+  // first visible tile at or after t (n if none)
+  __device__ __forceinline__ int next(int t) const {
+    if (t < a1) return t;
+    const int u = t > b0 ? t : b0;
+    return u < b1 ? u : n;
+  }
+  __device__ __forceinline__ bool mask_free(int t) const {
+    const int r0 = t * TK, r1 = r0 + TK;
+    if (r1 > len) return false;
+    if (r1 <= e0) return true;
+    const bool second_ok = r1 <= seg + e1;
+    if (r0 >= seg) return second_ok;
+    return e0 == seg && second_ok;  // straddles the runs: both parts unmasked
+  }
+};
+
 // Visibility of the keys of a tile to one query of position qlim (the lane's
 // query), for key offsets c + u where u is the lane's part of the offset and
 // c a compile-time constant: c + u must exist (< nvalid) and, when causal, sit
