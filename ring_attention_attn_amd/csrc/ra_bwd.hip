@@ -14,6 +14,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "ra_internal.h"
 #include "ra_tile.h"
 
@@ -209,23 +211,28 @@ __device__ __forceinline__ bf16x8 rows_operand(const bf16_t* rows_tile, const bf
   return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// (1) dQ, query-stationary: like the forward, a wave owns 32 query rows of one
-//     head and streams 64-key tiles. S^T = K Q^T and dP^T = V dO^T put a query
+// (1) dQ, query-stationary: a workgroup of 8 waves (two per SIMD) shares each
+//     64-key K/V tile (LDS-DMA, double-buffered, one barrier per tile); a wave
+//     owns 32 query rows of one head. S^T = K Q^T and dP^T = V dO^T put a query
 //     in each lane, so LSE and D are per-lane scalars; dS^T (bf16, 8
 //     consecutive keys per register chunk thanks to the sigma row order) is the
-//     B operand of dQ^T += K^T dS^T. dq_acc is read-modify-written once per row
-//     at the end: no atomics.
-template <int D, bool KTT>
-__global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams p, int hpw,
-                                                                     int n_qt, int rows_per_wg) {
+//     B operand of dQ^T += K^T dS^T, whose A operand is read transposed from
+//     the row-major K tile. K rows have a stride of 19 16-byte chunks (b128
+//     reads conflict-free, transposing reads nearly so), V rows 17. dq_acc is
+//     read-modify-written once per row at the end: no atomics.
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, int n_qt,
+                                                        int rows_per_wg) {
+  constexpr int NW = 8;
   constexpr int KT = 64;
-  constexpr int KSTR = D + 16;
-  constexpr int KTSTR = KT + 8;
+  constexpr int KSTR = D + 24;   // 19 (D=128) / 11 (D=64) chunks
+  constexpr int VSTR = D + 8;    // 17 / 9 chunks
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[KTT ? D * KTSTR : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[KT * KSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[KT * KSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[KT * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[KT * VSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -251,6 +258,16 @@ __global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams 
 
   const bf16_t* K = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
   const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
+
+  // stale LDS must hold finite values (0 * NaN would poison dQ)
+  for (int i = tid; i < KT * KSTR / 8; i += NW * 64) {
+    ((bf16x8*)sK0)[i] = bf16x8{};
+    ((bf16x8*)sK1)[i] = bf16x8{};
+  }
+  for (int i = tid; i < KT * VSTR / 8; i += NW * 64) {
+    ((bf16x8*)sV0)[i] = bf16x8{};
+    ((bf16x8*)sV1)[i] = bf16x8{};
+  }
 
   const int64_t qrow = row0 + l32;
   const bool qok = qrow < lq;
@@ -278,101 +295,102 @@ __global__ __launch_bounds__(256, RA_BWD_DQ_MINB) void bwd_dq_kernel(StepParams 
 #pragma unroll
   for (int db = 0; db < ND; ++db) qacc[db] = f32x16{};
 
-  const int n_kt = (int)((lk + KT - 1) / KT);
-  auto tile_bounds = [&](int t, int64_t& lo, int64_t& hi_) {
-    const int64_t k0 = (int64_t)t * KT;
-    seg_bounds(p.km, k0, k0 + KT < lk ? k0 + KT : lk, lo, hi_);
-  };
-  auto next_visible = [&](int t) {
-    while (t < n_kt) {
-      if (!p.causal) return t;
-      int64_t lo, hh;
-      tile_bounds(t, lo, hh);
-      if (lo <= gq_hi) return t;
-      ++t;
-    }
-    return t;
+  const KeyTiles<KT> kt_wg(p.km, p.causal, gq_lo, gq_hi);
+  const KeyTiles<KT> kt_w(p.km, p.causal, wq_lo, wq_hi);
+  const int n_kt = kt_wg.n;
+
+  DmaStage<KT, D, KSTR * 2, NW> kst;
+  DmaStage<KT, D, VSTR * 2, NW> vst;
+  kst.init(p.k_ss, wave, lane);
+  vst.init(p.v_ss, wave, lane);
+  auto stage = [&](int t, auto b) {
+    constexpr int B = decltype(b)::value;
+    kst.issue(K, p.k_ss, (int64_t)t * KT, lk, B ? sK1 : sK0);
+    vst.issue(V, p.v_ss, (int64_t)t * KT, lk, B ? sV1 : sV0);
   };
 
-  RowStage<KT, D, KSTR> ks, vs;
-  ColStage<KT, D, KTSTR> kts;
-  ks.init(p.k_ss, tid);
-  vs.init(p.v_ss, tid);
-  if (KTT) kts.init(p.k_ss, tid);
-  auto load_tile = [&](int t) {
-    ks.load(K, p.k_ss, (int64_t)t * KT, lk);
-    vs.load(V, p.v_ss, (int64_t)t * KT, lk);
-    if (KTT) kts.load(K, p.k_ss, (int64_t)t * KT, lk);
-  };
-  int t = next_visible(0);
-  if (t < n_kt) load_tile(t);
-  while (t < n_kt) {
-    __syncthreads();
-    ks.store(sK);
-    vs.store(sV);
-    if (KTT) kts.store(sKt);
-    __syncthreads();
-    const int tn = next_visible(t + 1);
-    if (tn < n_kt) load_tile(tn);
-    int64_t klo, khi;
-    tile_bounds(t, klo, khi);
-    const bool wave_skip = !wave_active || (p.causal && klo > wq_hi);
-    if (!wave_skip) {
-      const bool need_mask = (int64_t)(t + 1) * KT > lk || (p.causal && khi > wq_lo);
-      const TilePos tp(p.km, (int64_t)t * KT, KT);
-      bf16x8 dsk[2][2];
+  const int k_lane = srow * KSTR + 8 * hi;
+  const int v_lane = srow * VSTR + 8 * hi;
+  const int grp = lane >> 4, gi = lane & 15;
+  const int kt_lane = (8 * hi + (gi >> 2)) * KSTR + 16 * (grp & 1) + 4 * (gi & 3);
+
+  auto compute = [&](int t, auto b) {
+    constexpr int B = decltype(b)::value;
+    if (!wave_active) return;
+    const bf16_t* cK = (B ? sK1 : sK0);
+    const bf16_t* cV = (B ? sV1 : sV0);
+    // S^T = K Q^T and dP^T = V dO^T; register r of key block kb is key
+    // t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-        {
-          // chunk c+1's K and V operands load while chunk c's MFMAs run
-          bf16x8 ak[2], av[2];
-          auto ld = [&](int c, int slot) {
-            const int off = (kb * 32 + srow) * KSTR + 16 * c + 8 * hi;
-            ak[slot] = *(const bf16x8*)(sK + off);
-            av[slot] = *(const bf16x8*)(sV + off);
-          };
-          ld(0, 0);
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
-            sacc = mfma32(ak[c & 1], qreg[c], sacc);
-            pacc = mfma32(av[c & 1], doreg[c], pacc);
-          }
-        }
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          bf16x8 v8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * hf + e;
-            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -lse2));
-            if (need_mask) {
-              const int off = kb * 32 + 16 * hf + 8 * hi + e;
-              const bool vis = (off < tp.nvalid) & (tp.pos(off) <= qlim);
-              pr = vis ? pr : 0.f;
-            }
-            v8[e] = (bf16_t)(pr * (pacc[r] - dl));
-          }
-          dsk[kb][hf] = v8;
-        }
+        sacc[kb] = mfma32(*(const bf16x8*)(cK + k_lane + kb * 32 * KSTR + 16 * c), qreg[c], sacc[kb]);
+        pacc[kb] = mfma32(*(const bf16x8*)(cV + v_lane + kb * 32 * VSTR + 16 * c), doreg[c], pacc[kb]);
       }
-      {
-        // step i = (db, cc); step i+1's K^T operand loads while step i's MFMA runs
-        bf16x8 a[2];
-        a[0] = rows_operand<KTT, KSTR, KTSTR>(sK, sKt, 0, 0, lane);
+    if (!kt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
+      const TileRows tk(p.km, (int64_t)t * KT, KT);
+      const MaskBounds mb(tk, qlim, 8 * hi, p.causal);
 #pragma unroll
-        for (int i = 0; i < 4 * ND; ++i) {
-          if (i + 1 < 4 * ND)
-            a[(i + 1) & 1] = rows_operand<KTT, KSTR, KTSTR>(sK, sKt, 16 * ((i + 1) & 3),
-                                                            32 * ((i + 1) >> 2), lane);
-          const int db = i >> 2, cc = i & 3;
-          qacc[db] = mfma32(a[i & 1], dsk[cc >> 1][cc & 1], qacc[db]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool vis = mb.key_visible(kb * 32 + 16 * (r >> 3) + (r & 7));
+          sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
         }
-      }
     }
+    // dS = P (dP - D), P = exp2(S scale_log2 - LSE log2e), rounded to bf16
+    bf16x8 dsk[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hf + e;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2, -lse2));
+          v[e] = pr * (pacc[kb][r] - dl);
+        }
+        dsk[kb][hf] = pack_bf16x8(v);
+      }
+    // dQ^T += K^T dS^T: K^T operand = keys 16*cc + 8*hi .. +8 of d row
+    // 32*db + l32, read transposed; consecutive MFMAs use different accumulators
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16_t* a = cK + kt_lane + 16 * cc * KSTR + 32 * db;
+        const bf16x4 lo4 = ds_read_tr(a);
+        const bf16x4 hi4 = ds_read_tr(a + 4 * KSTR);
+        const bf16x8 ak = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        qacc[db] = mfma32(ak, dsk[cc >> 1][cc & 1], qacc[db]);
+      }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  __syncthreads();  // zero-fill done before any DMA lands
+  int t = kt_wg.next(0);
+  if (t < n_kt) stage(t, B0{});
+  // tiles alternate between two buffers; unrolled so each is a distinct array
+  while (t < n_kt) {
+    wait_vmem();
+    __syncthreads();  // tile t visible in buffer 0; every wave is done with buffer 1
+    int tn = kt_wg.next(t + 1);
+    if (tn < n_kt) stage(tn, B1{});
+    compute(t, B0{});
+    t = tn;
+    if (t >= n_kt) break;
+    wait_vmem();
+    __syncthreads();
+    tn = kt_wg.next(t + 1);
+    if (tn < n_kt) stage(tn, B0{});
+    compute(t, B1{});
     t = tn;
   }
+
   if (!qok) return;
   float* dq = p.o + qrow * p.o_ss + (int64_t)h * p.o_hs;
 #pragma unroll
@@ -655,11 +673,11 @@ template <int D>
 hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   if (p.qm.len > 0 && p.km.len > 0) {
     const int hpw = gcd_int(p.group, 4);
-    const int rows_per_wg = (4 / hpw) * 32;
+    const int rows_per_wg = (8 / hpw) * 32;
     const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
     const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, (bool)RA_BWD_KTT>), dim3((unsigned)grid), dim3(256), 0, s,
-                       p, hpw, n_qt, rows_per_wg);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw, n_qt,
+                       rows_per_wg);
   }
   const int n_kt = (int)((p.km.len + 127) / 128);
   const int64_t grid = (int64_t)p.hkv * n_kt;
