@@ -30,10 +30,6 @@
 #ifndef RA_BWD_QTT
 #define RA_BWD_QTT 0
 #endif
-// 1: dK/dV kernel reads its K^T/V^T operands from LDS instead of registers
-#ifndef RA_BWD_KVL
-#define RA_BWD_KVL 0
-#endif
 
 namespace {
 
@@ -195,22 +191,6 @@ __global__ __launch_bounds__(64) void bwd_dkv_simple_kernel(StepParams p) {
 }
 
 // ============================================================= MFMA kernels
-// Operand A of a product that contracts over rows of a tile held row-major in
-// LDS (K for dQ^T += K^T dS^T; Q, dO for dK^T, dV^T): 8 values per lane from
-// rows base + 8*hi + 0..7 at column col0 + l32 -- either one 16-byte read of a
-// transposed copy (TRANSPOSED) or two transposing reads of the row-major tile.
-template <bool TRANSPOSED, int RSTR, int TSTR>
-__device__ __forceinline__ bf16x8 rows_operand(const bf16_t* rows_tile, const bf16_t* cols_tile,
-                                               int base, int col0, int lane) {
-  const int l32 = lane & 31, hi = lane >> 5;
-  if (TRANSPOSED) return *(const bf16x8*)(cols_tile + (col0 + l32) * TSTR + base + 8 * hi);
-  const int grp = lane >> 4, gi = lane & 15;
-  const bf16_t* b = rows_tile + (base + 8 * hi + (gi >> 2)) * RSTR + col0 + 16 * (grp & 1) + 4 * (gi & 3);
-  const bf16x4 lo4 = ds_read_tr(b);
-  const bf16x4 hi4 = ds_read_tr(b + 4 * RSTR);
-  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // (1) dQ, query-stationary: a workgroup of 8 waves (two per SIMD) shares each
 //     64-key K/V tile (LDS-DMA, double-buffered, one barrier per tile); a wave
 //     owns 32 query rows of one head. S^T = K Q^T and dP^T = V dO^T put a query
@@ -405,36 +385,43 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     }
 }
 
-// (2) dK, dV, key-stationary: a workgroup of 4 waves owns 128 keys of one KV
-//     head (32 per wave; K^T and V^T B operands held in registers) and walks the
-//     64-row query tiles of every query head of the group. S = Q K^T and
-//     dP = dO V^T put a key in each lane (query rows fed in sigma order), so P
-//     and dS, rounded to bf16, are directly the B operands of dV^T += dO^T P and
-//     dK^T += Q^T dS. Each dK/dV element has one writer.
-template <int D, bool QTT, bool KVL>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
-  constexpr int KB = 128;
-  constexpr int QT = 64;
-  constexpr int QSTR = D + 16;
-  constexpr int QTSTR = QT + 8;
+// (2) dK, dV, key-stationary: a workgroup of 8 waves (two per SIMD) owns 128
+//     keys of one KV head and walks the 64-row query tiles of every query head
+//     of the group. The waves come in pairs on the same 32 keys: the P wave
+//     computes S = Q K^T (K held as the MFMA B operand), P = exp(S - LSE) and
+//     dV^T += dO^T P; it hands P (bf16) to its partner through LDS, which one
+//     step later computes dP = dO V^T (V held), dS = P (dP - D) and
+//     dK^T += Q^T dS. Each wave keeps one accumulator set, so both fit two
+//     waves per SIMD, and no product is computed twice. Q and dO tiles reach
+//     LDS by DMA in an XOR-swizzled layout (three rotating buffers, one barrier
+//     per step), with the tile's LSE (log2 units) and D. Query rows are fed in
+//     sigma order, so P and dS are directly B operands of the dV / dK
+//     products, whose A operands are read transposed from the same tiles.
+//     Each dK/dV element has one writer.
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
+  constexpr int NW = 8;
+  constexpr int KB = 128;  // keys per workgroup
+  constexpr int QT = 64;   // query rows per tile
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[QT * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sdO[QT * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[QTT ? D * QTSTR : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t sdOt[QTT ? D * QTSTR : 8];
-  __shared__ __attribute__((aligned(16))) float sL[QT];
-  __shared__ __attribute__((aligned(16))) float sDl[QT];
-  // KVL: the workgroup's 128 keys of K and V stay in LDS (row-major) and the
-  // B operands are read per use, which keeps vector registers free for
-  // in-flight operand loads
-  constexpr int KVSTR = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t sKk[KVL ? KB * KVSTR : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t sVv[KVL ? KB * KVSTR : 8];
+  constexpr int TB = QT * D;  // elements per Q / dO tile
+  constexpr int PB = QT * 32;  // elements of P per key group
+  __shared__ __attribute__((aligned(1024))) bf16_t sQ0[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sQ1[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sQ2[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sG0[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sG1[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sG2[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sP[2 * 4 * PB];  // two slots
+  __shared__ __attribute__((aligned(16))) float sL[3][QT];  // LSE * log2(e) (+inf: no contribution)
+  __shared__ __attribute__((aligned(16))) float sD[3][QT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const bool pwave = wave < 4;  // role: P / dV (else dS / dK)
+  const int kw = wave & 3;      // key group of the wave pair
   const int l32 = lane & 31, hi = lane >> 5;
   const int srow = sigma32(l32);
 
@@ -444,207 +431,246 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   const int64_t lq = p.qm.len, lk = p.km.len;
   const int64_t key0 = (int64_t)kt * KB;
   const int64_t key1 = key0 + KB < lk ? key0 + KB : lk;
-  const int64_t wkey0 = key0 + wave * 32;
+  const int64_t wkey0 = key0 + kw * 32;
   const int64_t mykey = wkey0 + l32;
   const bool key_ok = mykey < lk;
-  // first query position that sees this lane's key (never, for a missing key)
-  const int kmin = !key_ok ? INT_MAX : (p.causal ? (int)seg_pos(p.km, mykey) : INT_MIN);
-  int64_t gk_lo, gk_hi, wk_lo = INT64_MAX, wk_hi = INT64_MIN;
+  const int kpos = key_ok ? (int)seg_pos(p.km, mykey) : INT_MAX;
+  int64_t gk_lo, gk_hi, wk_lo = 0, wk_hi = 0;
   seg_bounds(p.km, key0, key1, gk_lo, gk_hi);
   const bool wave_has_keys = wkey0 < lk;
   if (wave_has_keys) seg_bounds(p.km, wkey0, wkey0 + 32 < lk ? wkey0 + 32 : lk, wk_lo, wk_hi);
 
-  bf16x8 kreg[KVL ? 1 : NC], vreg[KVL ? 1 : NC];
-  if (KVL) {
-    RowStage<KB, D, KVSTR> kst, vst;
-    kst.init(p.k_ss, tid);
-    vst.init(p.v_ss, tid);
-    kst.load((const bf16_t*)p.k + (int64_t)g * p.k_hs, p.k_ss, key0, lk);
-    vst.load((const bf16_t*)p.v + (int64_t)g * p.v_hs, p.v_ss, key0, lk);
-    kst.store(sKk);
-    vst.store(sVv);
-  } else {
-    const bf16_t* Kp = (const bf16_t*)p.k + (int64_t)g * p.k_hs + mykey * p.k_ss + 8 * hi;
-    const bf16_t* Vp = (const bf16_t*)p.v + (int64_t)g * p.v_hs + mykey * p.v_ss + 8 * hi;
+  // K (P wave) or V (dK wave) of this lane's key as the B operand: d = 16c + 8*hi .. +8
+  bf16x8 breg[NC];
+  {
+    const bf16_t* Bp = pwave ? (const bf16_t*)p.k + (int64_t)g * p.k_hs + mykey * p.k_ss
+                             : (const bf16_t*)p.v + (int64_t)g * p.v_hs + mykey * p.v_ss;
 #pragma unroll
-    for (int c = 0; c < (KVL ? 1 : NC); ++c) {
+    for (int c = 0; c < NC; ++c) {
       bf16x8 z = {};
-      kreg[c] = key_ok ? *(const bf16x8*)(Kp + 16 * c) : z;
-      vreg[c] = key_ok ? *(const bf16x8*)(Vp + 16 * c) : z;
+      breg[c] = key_ok ? *(const bf16x8*)(Bp + 8 * hi + 16 * c) : z;
     }
   }
-  const bf16_t* kop = sKk + (wave * 32 + l32) * KVSTR + 8 * hi;  // B operand rows (KVL)
-  const bf16_t* vop = sVv + (wave * 32 + l32) * KVSTR + 8 * hi;
-  f32x16 dkacc[ND], dvacc[ND];
+  f32x16 acc[ND];  // dV^T (P wave) or dK^T (dK wave): lane = key, registers = d
 #pragma unroll
-  for (int db = 0; db < ND; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
+  for (int db = 0; db < ND; ++db) acc[db] = f32x16{};
 
-  const int n_qt = (int)((lq + QT - 1) / QT);
-  const int n_it = p.group * n_qt;  // (head, query tile) iterations
-  auto tile_bounds = [&](int it, int64_t& lo, int64_t& hi_) {
-    const int64_t q0 = (int64_t)(it % n_qt) * QT;
-    seg_bounds(p.qm, q0, q0 + QT < lq ? q0 + QT : lq, lo, hi_);
-  };
-  auto next_visible = [&](int it) {
-    while (it < n_it) {
-      if (!p.causal) return it;
-      int64_t lo, hh;
-      tile_bounds(it, lo, hh);
-      if (hh >= gk_lo) return it;
-      ++it;
+  // iterations: (query head of the group hh, query tile t) pairs, hh-major;
+  // hh == group marks the end
+  const QueryTiles<QT> qt_wg(p.qm, p.causal, gk_lo, gk_hi);
+  const QueryTiles<QT> qt_w(p.qm, p.causal, wk_lo, wk_hi);
+  const int t_first = qt_wg.next(0);
+  // the visible tile after (hh, t), or (group, 0)
+  auto advance = [&](int& hh, int& t) {
+    t = qt_wg.next(t + 1);
+    if (t >= qt_wg.n) {
+      ++hh;
+      t = t_first;
     }
-    return it;
   };
 
-  RowStage<QT, D, QSTR> qs, ds;
-  ColStage<QT, D, QTSTR> qts, dts;
-  qs.init(p.q_ss, tid);
-  ds.init(p.do_ss, tid);
-  if (QTT) {
-    qts.init(p.q_ss, tid);
-    dts.init(p.do_ss, tid);
-  }
-  auto load = [&](int it) {
-    const int h = g * p.group + it / n_qt;
-    const int64_t q0 = (int64_t)(it % n_qt) * QT;
-    const bf16_t* Qh = (const bf16_t*)p.q + (int64_t)h * p.q_hs;
-    const bf16_t* Gh = (const bf16_t*)p.dout + (int64_t)h * p.do_hs;
-    qs.load(Qh, p.q_ss, q0, lq);
-    ds.load(Gh, p.do_ss, q0, lq);
-    if (QTT) {
-      qts.load(Qh, p.q_ss, q0, lq);
-      dts.load(Gh, p.do_ss, q0, lq);
-    }
+  DmaSwz<QT, D, NW> qst, gst;
+  qst.init(p.q_ss, wave, lane);
+  gst.init(p.do_ss, wave, lane);
+  auto qbuf = [&](auto b) -> bf16_t* {
+    constexpr int B = decltype(b)::value;
+    return B == 0 ? sQ0 : (B == 1 ? sQ1 : sQ2);
   };
-  int it = lq > 0 ? next_visible(0) : n_it;
-  if (it < n_it) load(it);
-  while (it < n_it) {
-    const int h = g * p.group + it / n_qt;
-    const int64_t q0 = (int64_t)(it % n_qt) * QT;
-    __syncthreads();
-    qs.store(sQ);
-    ds.store(sdO);
-    if (QTT) {
-      qts.store(sQt);
-      dts.store(sdOt);
-    }
-    if (tid < QT) {
-      const int64_t row = q0 + tid;
-      float l2 = INFINITY, dl = 0.f;
+  auto gbuf = [&](auto b) -> bf16_t* {
+    constexpr int B = decltype(b)::value;
+    return B == 0 ? sG0 : (B == 1 ? sG1 : sG2);
+  };
+  // LSE and D of a tile: wave 0 loads them into registers when the tile's DMA
+  // is issued and writes them to LDS after its compute of that step
+  float ld_l = INFINITY, ld_d = 0.f;
+  auto stage = [&](int hh, int t, auto b) {
+    const int h = g * p.group + hh;
+    const int64_t q0 = (int64_t)t * QT;
+    qst.issue((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, q0, lq, qbuf(b));
+    gst.issue((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, q0, lq, gbuf(b));
+    if (wave == 0) {
+      const int64_t row = q0 + lane;
+      ld_l = INFINITY;
+      ld_d = 0.f;
       if (row < lq) {
-        const float lse = p.lse_in[(int64_t)h * lq + row];
-        l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;  // empty row: no contribution
-        dl = p.delta[(int64_t)h * lq + row];
+        const float l = p.lse_in[(int64_t)h * lq + row];
+        ld_l = l == -INFINITY ? INFINITY : l * kLog2e;  // empty row: no contribution
+        ld_d = p.delta[(int64_t)h * lq + row];
       }
-      sL[tid] = l2;
-      sDl[tid] = dl;
     }
-    __syncthreads();
-    const int itn = next_visible(it + 1);
-    if (itn < n_it) load(itn);
+  };
+  auto store_ld = [&](auto b) {
+    constexpr int B = decltype(b)::value;
+    if (wave == 0) {
+      sL[B][lane] = ld_l;
+      sD[B][lane] = ld_d;
+    }
+  };
 
-    int64_t tq_lo, tq_hi;
-    tile_bounds(it, tq_lo, tq_hi);
-    const bool wave_skip = !wave_has_keys || (p.causal && tq_hi < wk_lo);
-    if (!wave_skip) {
-      const bool need_mask = (wkey0 + 32 > lk) || q0 + QT > lq || (p.causal && wk_hi > tq_lo);
-      const TilePos tp(p.qm, q0, QT);
-      // S and dP of both 32-query blocks are issued first; block 0's softmax
-      // then runs on the vector ALU while block 1's MFMAs execute, and block 1's
-      // softmax while block 0's dV/dK MFMAs execute
-      f32x16 sacc[2], pacc[2];
+  // per-lane byte offsets in a swizzled tile: 16-byte row reads of chunk
+  // 2*c + hi of row qb*32 + sigma(l32), and transposing reads of rows
+  // 16*cq + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3)
+  int roff[NC];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
-        // operands of chunk c+1 are loaded while chunk c's MFMAs run
-        bf16x8 aq[2], ao[2], bk[2], bv[2];
-        auto ld = [&](int c, int slot) {
-          const int off = (qb * 32 + srow) * QSTR + 16 * c + 8 * hi;
-          aq[slot] = *(const bf16x8*)(sQ + off);
-          ao[slot] = *(const bf16x8*)(sdO + off);
-          bk[slot] = KVL ? *(const bf16x8*)(kop + 16 * c) : kreg[KVL ? 0 : c];
-          bv[slot] = KVL ? *(const bf16x8*)(vop + 16 * c) : vreg[KVL ? 0 : c];
-        };
-        ld(0, 0);
+  for (int c = 0; c < NC; ++c) roff[c] = swz_off<D>(srow, 2 * c + hi);
+  const int grp = lane >> 4, gi = lane & 15;
+  int toff[2][ND];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if (c + 1 < NC) ld(c + 1, (c + 1) & 1);
-          sacc[qb] = mfma32(aq[c & 1], bk[c & 1], sacc[qb]);
-          pacc[qb] = mfma32(ao[c & 1], bv[c & 1], pacc[qb]);
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      toff[sh][db] = swz_off<D>(8 * hi + (gi >> 2) + 4 * sh, 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1)) +
+                     8 * (gi & 1);
+  // P hand-off slot of this lane: block (qb, hf) of key group kw, 16 bytes per lane
+  const int p_lane = kw * PB + lane * 8;
+
+  // A x (B operand) over the tile's two 32-row query blocks: register r of
+  // block qb is query row qb*32 + 16*(r/8) + 8*hi + r%8, the lane's key
+  auto row_products = [&](const char* tile, f32x16 (&x)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      x[qb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        x[qb] = mfma32(*(const bf16x8*)(tile + qb * 32 * 2 * D + roff[c]), breg[c], x[qb]);
+    }
+  };
+  // acc^T += tile^T B' over 16 query rows cq (B' = P or dS chunk in bf16)
+  auto col_products = [&](const char* tile, int cq, const bf16x8& bv) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const char* a = tile + 16 * cq * 2 * D;
+      const bf16x8 av = __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + toff[0][db])),
+                                                ds_read_tr((const bf16_t*)(a + toff[1][db])), 0,
+                                                1, 2, 3, 4, 5, 6, 7);
+      acc[db] = mfma32(av, bv, acc[db]);
+    }
+  };
+
+  // P wave, tile `it` in buffer b: S, mask, P -> LDS slot ps, dV^T += dO^T P
+  auto p_step = [&](int t, auto b, int ps) {
+    constexpr int B = decltype(b)::value;
+    const char* cQ = (const char*)qbuf(b);
+    const char* cG = (const char*)gbuf(b);
+    f32x16 sacc[2];
+    row_products(cQ, sacc);
+    if (!qt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
+      const TileRows tq(p.qm, (int64_t)t * QT, QT);
+      const QMaskBounds mb(tq, kpos, key_ok, 8 * hi, p.causal);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool vis = mb.row_visible(qb * 32 + 16 * (r >> 3) + (r & 7));
+          sacc[qb][r] = vis ? sacc[qb][r] : -INFINITY;
         }
+    }
+    bf16_t* sp = sP + ps * 4 * PB + p_lane;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int qo = qb * 32 + 16 * hf + 8 * hi;
+        const f32x4 la = *(const f32x4*)(&sL[B][qo]), lb = *(const f32x4*)(&sL[B][qo + 4]);
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l2 = e < 4 ? la[e] : lb[e - 4];
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * hf + e], p.scale_log2, -l2));
+        }
+        const bf16x8 pk = pack_bf16x8(pv);
+        *(bf16x8*)(sp + (2 * qb + hf) * 512) = pk;
+        col_products(cG, 2 * qb + hf, pk);
       }
+  };
+  // dK wave, tile `it` in buffer b with its P in slot ps: dP, dS, dK^T += Q^T dS
+  auto k_step = [&](auto b, int ps) {
+    constexpr int B = decltype(b)::value;
+    const char* cQ = (const char*)qbuf(b);
+    const char* cG = (const char*)gbuf(b);
+    f32x16 pacc[2];
+    row_products(cG, pacc);
+    const bf16_t* sp = sP + ps * 4 * PB + p_lane;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // register r is query q0 + qb*32 + 16*(r/8) + 8*hi + r%8
-        bf16x8 pP[2], pS[2];
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int qo = qb * 32 + 16 * hf + 8 * hi;
-          const f32x4 la = *(const f32x4*)(sL + qo), lb = *(const f32x4*)(sL + qo + 4);
-          const f32x4 da = *(const f32x4*)(sDl + qo), db_ = *(const f32x4*)(sDl + qo + 4);
-          bf16x8 p8, s8;
+      for (int hf = 0; hf < 2; ++hf) {
+        const int qo = qb * 32 + 16 * hf + 8 * hi;
+        const f32x4 da = *(const f32x4*)(&sD[B][qo]), db_ = *(const f32x4*)(&sD[B][qo + 4]);
+        const bf16x8 pk = *(const bf16x8*)(sp + (2 * qb + hf) * 512);
+        float sv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * hf + e;
-            const float l2 = e < 4 ? la[e] : lb[e - 4];
-            const float dl = e < 4 ? da[e] : db_[e - 4];
-            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], p.scale_log2, -l2));
-            if (need_mask) {
-              const bool vis = (qo + e < tp.nvalid) & (tp.pos(qo + e) >= kmin);
-              pr = vis ? pr : 0.f;
-            }
-            p8[e] = (bf16_t)pr;
-            s8[e] = (bf16_t)(pr * (pacc[qb][r] - dl));
-          }
-          pP[hf] = p8;
-          pS[hf] = s8;
+        for (int e = 0; e < 8; ++e) {
+          const float dl = e < 4 ? da[e] : db_[e - 4];
+          sv[e] = (float)pk[e] * (pacc[qb][8 * hf + e] - dl);
         }
-        // (db, hf) step i+1's transposed operands load while step i's MFMAs run
-        bf16x8 ao[2], aq[2];
-        auto ld = [&](int i, int slot) {
-          const int db = i >> 1, cc = 2 * qb + (i & 1);
-          ao[slot] = rows_operand<QTT, QSTR, QTSTR>(sdO, sdOt, 16 * cc, 32 * db, lane);
-          aq[slot] = rows_operand<QTT, QSTR, QTSTR>(sQ, sQt, 16 * cc, 32 * db, lane);
-        };
-        ld(0, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * ND; ++i) {
-          if (i + 1 < 2 * ND) ld(i + 1, (i + 1) & 1);
-          const int db = i >> 1, hf = i & 1;
-          dvacc[db] = mfma32(ao[i & 1], pP[hf], dvacc[db]);
-          dkacc[db] = mfma32(aq[i & 1], pS[hf], dkacc[db]);
-        }
+        col_products(cQ, 2 * qb + hf, pack_bf16x8(sv));
+      }
+  };
+
+  // Step i: tile i is in buffer i % 3, tile i - 1 in buffer (i - 1) % 3; the
+  // DMA of tile i + 1 goes to buffer (i + 1) % 3 (last read at step i - 2).
+  // P waves compute tile i (P into slot i % 2); dK waves compute tile i - 1.
+  // The two roles run separate loops with the same barrier sequence, so each
+  // role's registers are allocated on their own.
+  int ch = t_first < qt_wg.n ? 0 : p.group, ct = t_first;  // tile i
+  int slot = 0;                                            // P slot of tile i
+  bool have_prev = false;
+  auto step = [&](auto bc, auto bp, auto bn, auto role) {
+    constexpr bool PW = decltype(role)::value;
+    wait_vmem();
+    __syncthreads();  // tile i visible (with LSE/D); P of tile i-1 visible; buffer bn free
+    const bool cur = ch < p.group;
+    int nh = ch, nt = ct;
+    if (cur) advance(nh, nt);
+    const bool nxt = nh < p.group;
+    if (nxt) stage(nh, nt, bn);
+    if (wave_has_keys) {
+      if (PW) {
+        if (cur) p_step(ct, bc, slot);
+      } else if (have_prev) {
+        k_step(bp, slot ^ 1);
       }
     }
-    it = itn;
+    if (nxt) store_ld(bn);  // becomes visible at the next step's barrier
+    have_prev = cur;
+    ch = nh;
+    ct = nt;
+    slot ^= 1;
+    return have_prev;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  if (ch < p.group) {
+    stage(ch, ct, B0{});
+    store_ld(B0{});
+    // three-step unroll: buffer indices are compile-time constants
+    if (pwave) {
+      const std::true_type r{};
+      while (step(B0{}, B2{}, B1{}, r) && step(B1{}, B0{}, B2{}, r) && step(B2{}, B1{}, B0{}, r)) {
+      }
+    } else {
+      const std::false_type r{};
+      while (step(B0{}, B2{}, B1{}, r) && step(B1{}, B0{}, B2{}, r) && step(B2{}, B1{}, B0{}, r)) {
+      }
+    }
   }
 
   // ---- epilogue: lanes = keys, registers = d rows 8*(r/4) + 4*hi + r%4
   if (!key_ok) return;
-  float* dkp = p.dk + mykey * p.dk_ss + (int64_t)g * p.dk_hs;
-  float* dvp = p.dv + mykey * p.dk_ss + (int64_t)g * p.dk_hs;
+  float* dst = (pwave ? p.dv : p.dk) + mykey * p.dk_ss + (int64_t)g * p.dk_hs;
+  const float sc = pwave ? 1.f : p.scale;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x4 a, b;
+      f32x4 a;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] = dkacc[db][4 * i + j] * p.scale;
-        b[j] = dvacc[db][4 * i + j];
-      }
-      f32x4* pa = (f32x4*)(dkp + 32 * db + 8 * i + 4 * hi);
-      f32x4* pb = (f32x4*)(dvp + 32 * db + 8 * i + 4 * hi);
-      if (p.dkv_accumulate) {
-        a += *pa;
-        b += *pb;
-      }
+      for (int j = 0; j < 4; ++j) a[j] = acc[db][4 * i + j] * sc;
+      f32x4* pa = (f32x4*)(dst + 32 * db + 8 * i + 4 * hi);
+      if (p.dkv_accumulate) a += *pa;
       *pa = a;
-      *pb = b;
     }
 }
 
@@ -682,8 +708,7 @@ hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   const int n_kt = (int)((p.km.len + 127) / 128);
   const int64_t grid = (int64_t)p.hkv * n_kt;
   if (grid > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, (bool)RA_BWD_QTT, (bool)RA_BWD_KVL>), dim3((unsigned)grid),
-                       dim3(256), 0, s, p, n_kt);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, n_kt);
   return hipGetLastError();
 }
 

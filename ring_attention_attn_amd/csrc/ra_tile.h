@@ -200,6 +200,58 @@ struct DmaStage {
   }
 };
 
+// ---- XOR-swizzled row-major tiles (no padding): rows of D bf16, 16-byte
+// chunk c of row r stored at chunk c ^ swz(r). Reads of one chunk from 16
+// consecutive rows (16-byte loads) and transposing reads of 4 rows x 64 bytes
+// both hit distinct banks (64 banks of 4 bytes: 16 chunk slots per 256 bytes).
+template <int D>
+__host__ __device__ __forceinline__ int swz(int r) {
+  if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  const int j = r >> 1;  // D == 64: two rows per 256 bytes
+  return 4 * (j & 1) + ((j >> 1) & 3);
+}
+// byte offset of chunk c of row r
+template <int D>
+__host__ __device__ __forceinline__ int swz_off(int r, int c) {
+  return r * 2 * D + 16 * (c ^ swz<D>(r));
+}
+
+// LDS-DMA staging of a T x D bf16 tile into the swizzled layout: instruction j
+// fills bytes [1024 j, 1024 j + 1024); lane i writes physical chunk slot
+// (16 i % (2D)) / 16 of row (1024 j + 16 i) / (2D), loading the logical chunk
+// that the swizzle maps there.
+template <int T, int D, int NW>
+struct DmaSwz {
+  static constexpr int NJ = T * 2 * D / 1024;
+  static constexpr int PER = (NJ + NW - 1) / NW;
+  static_assert(T * 2 * D % 1024 == 0, "whole 1 KiB blocks");
+  uint32_t voff[PER];
+  int wave;
+  __device__ __forceinline__ void init(int64_t ss, int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int pb = 1024 * (wave + k * NW) + 16 * lane;
+      int row = pb / (2 * D);
+      const int phys = (pb % (2 * D)) / 16;
+      row = row < T ? row : 0;
+      const int c = phys ^ swz<D>(row);
+      voff[k] = (uint32_t)(((int64_t)row * ss + 8 * c) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16_t* base, int64_t ss, int64_t row0,
+                                        int64_t nrows, bf16_t* lds) const {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = wave + k * NW;
+      if (j < NJ)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((char*)lds + 1024 * j), 16,
+                                                 voff[k], 0, 0, 0);
+    }
+  }
+};
+
 // Wait until this wave's outstanding vector-memory operations (LDS-DMA loads
 // included) are complete.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
@@ -321,6 +373,80 @@ struct MaskBounds {
   }
   __device__ __forceinline__ bool key_visible(int c) const {
     return (c < nv) & (c <= (c < sp ? a0 : a1));
+  }
+};
+
+// Query tiles of TQ rows as seen by a block of keys (positions [k_first,
+// k_last]), in int32: tiles holding a query at or after k_first (visible: the
+// suffixes [a0, a1) of the first run and [b0, n) of the second), and whether a
+// tile has only existing rows at positions >= k_last (mask-free).
+template <int TQ>
+struct QueryTiles {
+  int n, len, seg, a0, a1, b0, f0, f1;
+  __device__ __forceinline__ QueryTiles(const SegMap& qm, int causal, int64_t k_first,
+                                        int64_t k_last) {
+    len = (int)qm.len;
+    seg = (int)qm.seg_len;
+    n = (len + TQ - 1) / TQ;
+    const int64_t n1 = qm.len - qm.seg_len;
+    if (causal) {
+      // first row of each run at a position >= x
+      auto from = [&](int64_t x, int& r0, int& r1) {
+        const int64_t a = x - qm.pos0, b = x - qm.pos1;
+        r0 = (int)(a < 0 ? 0 : (a > qm.seg_len ? qm.seg_len : a));
+        r1 = (int)(b < 0 ? 0 : (b > n1 ? n1 : b));
+      };
+      int r0, r1;
+      from(k_first, r0, r1);
+      a0 = r0 / TQ;
+      a1 = r0 < seg ? (seg + TQ - 1) / TQ : a0;
+      b0 = (seg + r1) / TQ;
+      if (seg + r1 >= len) b0 = n;
+      from(k_last, f0, f1);
+    } else {
+      a0 = 0;
+      a1 = n;
+      b0 = n;
+      f0 = 0;
+      f1 = 0;
+    }
+  }
+  __device__ __forceinline__ int next(int t) const {
+    if (t < a0) t = a0;
+    if (t < a1) return t;
+    return t > b0 ? (t < n ? t : n) : (b0 < n ? b0 : n);
+  }
+  __device__ __forceinline__ bool mask_free(int t) const {
+    const int r0 = t * TQ, r1 = r0 + TQ;
+    if (r1 > len) return false;
+    if (r1 <= seg) return r0 >= f0;
+    if (r0 >= seg) return r0 >= seg + f1;
+    return r0 >= f0 && f1 == 0;  // straddles the runs
+  }
+};
+
+// Visibility of a tile's query rows to the lane's key (position kpos), for
+// query offsets c + u (u = the lane's part, c a compile-time constant): the row
+// must exist (< nvalid) and, when causal, sit at a position >= kpos. A key
+// that does not exist sees nothing.
+struct QMaskBounds {
+  int nv, sp, a0, a1;
+  __device__ __forceinline__ QMaskBounds(const TileRows& t, int kpos, bool key_ok, int u,
+                                         int causal) {
+    nv = t.nvalid - u;
+    sp = t.split - u;
+    if (!key_ok) {
+      a0 = a1 = INT_MAX;
+    } else if (causal) {
+      const int64_t x0 = (int64_t)kpos - t.base0 - u, x1 = (int64_t)kpos - t.base1 - u;
+      a0 = x0 > INT_MAX ? INT_MAX : (x0 < INT_MIN ? INT_MIN : (int)x0);
+      a1 = x1 > INT_MAX ? INT_MAX : (x1 < INT_MIN ? INT_MIN : (int)x1);
+    } else {
+      a0 = a1 = INT_MIN;
+    }
+  }
+  __device__ __forceinline__ bool row_visible(int c) const {
+    return (c < nv) & (c >= (c < sp ? a0 : a1));
   }
 };
 
