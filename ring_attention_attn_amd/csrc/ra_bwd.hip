@@ -547,14 +547,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     }
   };
 
+
   // P wave, tile `it` in buffer b: S, mask, P -> LDS slot ps, dV^T += dO^T P
-  auto p_step = [&](int t, auto b, int ps) {
+  auto p_step = [&](int t, auto b, int ps, auto mask_tag) {
     constexpr int B = decltype(b)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
     const char* cQ = (const char*)qbuf(b);
     const char* cG = (const char*)gbuf(b);
     f32x16 sacc[2];
     row_products(cQ, sacc);
-    if (!qt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
+    if (MASK) {  // branch-free masking of the diagonal / ragged tiles
       const TileRows tq(p.qm, (int64_t)t * QT, QT);
       const QMaskBounds mb(tq, kpos, key_ok, 8 * hi, p.causal);
 #pragma unroll
@@ -627,7 +629,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     if (nxt) stage(nh, nt, bn);
     if (wave_has_keys) {
       if (PW) {
-        if (cur) p_step(ct, bc, slot);
+        if (cur) {
+          if (qt_w.mask_free(ct))
+            p_step(ct, bc, slot, std::false_type{});
+          else
+            p_step(ct, bc, slot, std::true_type{});
+        }
       } else if (have_prev) {
         k_step(bp, slot ^ 1);
       }
