@@ -56,7 +56,8 @@ def build(verbose=False, out=OUT, src_dir=CSRC, build_dir=BUILD, extra_flags=())
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra_flags), srcs))
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    # -z defs: an unresolved symbol (e.g. a kernel launch stub) fails the build
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -197,22 +197,21 @@ __global__ __launch_bounds__(64) void bwd_dkv_simple_kernel(StepParams p) {
 //     in each lane, so LSE and D are per-lane scalars; dS^T (bf16, 8
 //     consecutive keys per register chunk thanks to the sigma row order) is the
 //     B operand of dQ^T += K^T dS^T, whose A operand is read transposed from
-//     the row-major K tile. K rows have a stride of 19 16-byte chunks (b128
-//     reads conflict-free, transposing reads nearly so), V rows 17. dq_acc is
-//     read-modify-written once per row at the end: no atomics.
+//     the row-major K tile. Both tiles use the XOR-swizzled layout, so the
+//     16-byte row reads and the transposing reads are free of bank conflicts.
+//     dq_acc is read-modify-written once per row at the end: no atomics.
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, int n_qt,
                                                         int rows_per_wg) {
   constexpr int NW = 8;
   constexpr int KT = 64;
-  constexpr int KSTR = D + 24;   // 19 (D=128) / 11 (D=64) chunks
-  constexpr int VSTR = D + 8;    // 17 / 9 chunks
+  constexpr int TB = KT * D;     // elements per K / V tile
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(1024))) bf16_t sK0[KT * KSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sK1[KT * KSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV0[KT * VSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV1[KT * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,11 +239,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
 
   // stale LDS must hold finite values (0 * NaN would poison dQ)
-  for (int i = tid; i < KT * KSTR / 8; i += NW * 64) {
+  for (int i = tid; i < TB / 8; i += NW * 64) {
     ((bf16x8*)sK0)[i] = bf16x8{};
     ((bf16x8*)sK1)[i] = bf16x8{};
-  }
-  for (int i = tid; i < KT * VSTR / 8; i += NW * 64) {
     ((bf16x8*)sV0)[i] = bf16x8{};
     ((bf16x8*)sV1)[i] = bf16x8{};
   }
@@ -279,8 +276,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   const KeyTiles<KT> kt_w(p.km, p.causal, wq_lo, wq_hi);
   const int n_kt = kt_wg.n;
 
-  DmaStage<KT, D, KSTR * 2, NW> kst;
-  DmaStage<KT, D, VSTR * 2, NW> vst;
+  DmaSwz<KT, D, NW, 1> kst, vst;
   kst.init(p.k_ss, wave, lane);
   vst.init(p.v_ss, wave, lane);
   auto stage = [&](int t, auto b) {
@@ -289,16 +285,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     vst.issue(V, p.v_ss, (int64_t)t * KT, lk, B ? sV1 : sV0);
   };
 
-  const int k_lane = srow * KSTR + 8 * hi;
-  const int v_lane = srow * VSTR + 8 * hi;
+  // per-lane byte offsets in a swizzled tile: 16-byte row reads of chunk
+  // 2*c + hi of row kb*32 + sigma(l32), and transposing reads of rows
+  // 16*cc + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3)
+  int roff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) roff[c] = swz_off<D>(srow, 2 * c + hi);
   const int grp = lane >> 4, gi = lane & 15;
-  const int kt_lane = (8 * hi + (gi >> 2)) * KSTR + 16 * (grp & 1) + 4 * (gi & 3);
+  int toff[2][ND];
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      toff[sh][db] = swz_off<D>(8 * hi + (gi >> 2) + 4 * sh, 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1)) +
+                     8 * (gi & 1);
 
   auto compute = [&](int t, auto b) {
     constexpr int B = decltype(b)::value;
     if (!wave_active) return;
-    const bf16_t* cK = (B ? sK1 : sK0);
-    const bf16_t* cV = (B ? sV1 : sV0);
+    const char* cK = (const char*)(B ? sK1 : sK0);
+    const char* cV = (const char*)(B ? sV1 : sV0);
     // S^T = K Q^T and dP^T = V dO^T; register r of key block kb is key
     // t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
     f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
@@ -306,8 +312,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = mfma32(*(const bf16x8*)(cK + k_lane + kb * 32 * KSTR + 16 * c), qreg[c], sacc[kb]);
-        pacc[kb] = mfma32(*(const bf16x8*)(cV + v_lane + kb * 32 * VSTR + 16 * c), doreg[c], pacc[kb]);
+        const int o = kb * 32 * 2 * D + roff[c];
+        sacc[kb] = mfma32(*(const bf16x8*)(cK + o), qreg[c], sacc[kb]);
+        pacc[kb] = mfma32(*(const bf16x8*)(cV + o), doreg[c], pacc[kb]);
       }
     if (!kt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
       const TileRows tk(p.km, (int64_t)t * KT, KT);
@@ -341,9 +348,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16_t* a = cK + kt_lane + 16 * cc * KSTR + 32 * db;
-        const bf16x4 lo4 = ds_read_tr(a);
-        const bf16x4 hi4 = ds_read_tr(a + 4 * KSTR);
+        const char* a = cK + 16 * cc * 2 * D;
+        const bf16x4 lo4 = ds_read_tr((const bf16_t*)(a + toff[0][db]));
+        const bf16x4 hi4 = ds_read_tr((const bf16_t*)(a + toff[1][db]));
         const bf16x8 ak = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         qacc[db] = mfma32(ak, dsk[cc >> 1][cc & 1], qacc[db]);
       }
@@ -469,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     }
   };
 
-  DmaSwz<QT, D, NW> qst, gst;
+  DmaSwz<QT, D, NW, 2> qst, gst;
   qst.init(p.q_ss, wave, lane);
   gst.init(p.do_ss, wave, lane);
   auto qbuf = [&](auto b) -> bf16_t* {

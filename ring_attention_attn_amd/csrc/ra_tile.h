@@ -220,7 +220,9 @@ __host__ __device__ __forceinline__ int swz_off(int r, int c) {
 // fills bytes [1024 j, 1024 j + 1024); lane i writes physical chunk slot
 // (16 i % (2D)) / 16 of row (1024 j + 16 i) / (2D), loading the logical chunk
 // that the swizzle maps there.
-template <int T, int D, int NW>
+// TAG only makes each kernel's instantiation distinct: with one shared
+// specialization, hipcc left a kernel's host launch stub undefined.
+template <int T, int D, int NW, int TAG>
 struct DmaSwz {
   static constexpr int NJ = T * 2 * D / 1024;
   static constexpr int PER = (NJ + NW - 1) / NW;
