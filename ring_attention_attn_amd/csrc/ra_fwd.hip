@@ -117,27 +117,25 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 // (one barrier per tile). The loop is software-pipelined: while the softmax and
 // O^T += V^T P^T of tile t run, the 16 MFMAs of S^T for the next tile are
 // issued in the same basic block, so vector and matrix work overlap inside
-// each wave. K rows are read with 16-byte loads (row stride of an odd number
-// of 16-byte chunks: conflict-free), V^T operands with ds_read_b64_tr_b16 (row
-// stride 20 (D = 128) or 12 (D = 64) chunks: conflict-free). Diagonal tiles
-// and ragged tails add one branch-free masking block.
+// each wave. Tiles use the XOR-swizzled row layout: K rows are read with
+// 16-byte loads and V^T operands with ds_read_b64_tr_b16, both free of bank
+// conflicts. Diagonal tiles and ragged tails add one branch-free masking block.
 template <int D>
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
                                                           int rows_per_wg) {
   constexpr int NW = 8;            // waves per workgroup
   constexpr int KT = 64;           // keys per LDS tile
-  constexpr int KSTR = D + 8;      // sK row stride (elements): odd number of 16-byte chunks
-  constexpr int VSTR = D + 32;     // sV row stride: 20 (D=128) / 12 (D=64) chunks
+  constexpr int TB = KT * D;       // elements per K / V tile (XOR-swizzled rows, no padding)
   constexpr int NC = D / 16;       // 16-wide d chunks (QK^T contraction steps)
   constexpr int ND = D / 32;       // 32-wide d blocks of O^T
   // log2-domain headroom before the running max is moved: P stays <= 2^8
   constexpr float kThresh = 8.f;
-  __shared__ __attribute__((aligned(1024))) bf16_t sK0[KT * KSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sK1[KT * KSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sK2[KT * KSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV0[KT * VSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV1[KT * VSTR];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV2[KT * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK2[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV2[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -168,12 +166,10 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
 
   // stale LDS must hold finite values: keys past the end are never read into
   // P != 0, but 0 * NaN would poison O
-  for (int i = tid; i < KT * KSTR / 8; i += NW * 64) {
+  for (int i = tid; i < TB / 8; i += NW * 64) {
     ((bf16x8*)sK0)[i] = bf16x8{};
     ((bf16x8*)sK1)[i] = bf16x8{};
     ((bf16x8*)sK2)[i] = bf16x8{};
-  }
-  for (int i = tid; i < KT * VSTR / 8; i += NW * 64) {
     ((bf16x8*)sV0)[i] = bf16x8{};
     ((bf16x8*)sV1)[i] = bf16x8{};
     ((bf16x8*)sV2)[i] = bf16x8{};
@@ -206,8 +202,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   const int n_kt = kt_wg.n;
   auto next_visible = [&](int t) { return kt_wg.next(t); };
 
-  DmaStage<KT, D, KSTR * 2, NW> kst;
-  DmaStage<KT, D, VSTR * 2, NW> vst;
+  DmaSwz<KT, D, NW, 0> kst, vst;
   kst.init(p.k_ss, wave, lane);
   vst.init(p.v_ss, wave, lane);
   auto kbuf = [&](auto b) -> bf16_t* {
@@ -224,21 +219,32 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   };
 
   // per-lane LDS offsets (elements); everything else is an immediate offset
-  const int k_lane = srow * KSTR + 8 * hi;
+  // per-lane byte offsets in a swizzled tile: 16-byte reads of chunk 2*c + hi
+  // of row kb*32 + sigma(l32) (K), and transposing reads of rows
+  // 16*cc + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3) (V)
+  int koff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = swz_off<D>(srow, 2 * c + hi);
   const int grp = lane >> 4, gi = lane & 15;
-  const int v_lane = (8 * hi + (gi >> 2)) * VSTR + 16 * (grp & 1) + 4 * (gi & 3);
+  int voff[2][ND];
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      voff[sh][db] = swz_off<D>(8 * hi + (gi >> 2) + 4 * sh, 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1)) +
+                     8 * (gi & 1);
 
   // S^T = K Q^T of the tile in buffer b; register r of key block kb is key
   // t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
   auto scores = [&](auto b, f32x16 (&sacc)[2]) {
-    const bf16_t* cK = kbuf(b) + k_lane;
+    const char* cK = (const char*)kbuf(b);
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = mfma32(*(const bf16x8*)(cK + kb * 32 * KSTR + 16 * c), qreg[c], sacc[kb]);
+        sacc[kb] = mfma32(*(const bf16x8*)(cK + kb * 32 * 2 * D + koff[c]), qreg[c], sacc[kb]);
   };
   // mask scores of tile t for this wave's queries (keys past the end, and
   // causally later keys) and move the exponent shift if the tile needs it
@@ -300,14 +306,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
         pk[kb][hf] = pack_bf16x8(pe);
       }
     l_run += rs0 + rs1;
-    const bf16_t* cV = vbuf(b) + v_lane;
+    const char* cV = (const char*)vbuf(b);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16_t* a = cV + 16 * cc * VSTR + 32 * db;
-        const bf16x4 lo4 = ds_read_tr(a);
-        const bf16x4 hi4 = ds_read_tr(a + 4 * VSTR);
+        const char* a = cV + 16 * cc * 2 * D;
+        const bf16x4 lo4 = ds_read_tr((const bf16_t*)(a + voff[0][db]));
+        const bf16x4 hi4 = ds_read_tr((const bf16_t*)(a + voff[1][db]));
         const bf16x8 av = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = mfma32(av, pk[cc >> 1][cc & 1], oacc[db]);
       }

@@ -257,6 +257,12 @@ struct DmaSwz {
 // Wait until this wave's outstanding vector-memory operations (LDS-DMA loads
 // included) are complete.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+// ... until at most N (< 16) of them are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x3f70 | N);
+}
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
