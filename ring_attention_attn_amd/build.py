@@ -35,9 +35,15 @@ def sources(src_dir=CSRC):
     return sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir) if f.endswith(".hip"))
 
 
-def _compile(src, verbose, build_dir, extra):
+def _compile(src, verbose, build_dir, extra, drop=()):
     obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + list(extra) + ["-c", src, "-o", obj]
+    flags = list(CFLAGS)
+    for d in drop:  # drop a flag and its argument list entry, e.g. ("-mllvm", "-amdgpu-...")
+        for i in range(len(flags) - len(d) + 1):
+            if tuple(flags[i:i + len(d)]) == tuple(d):
+                del flags[i:i + len(d)]
+                break
+    cmd = [HIPCC] + flags + list(extra) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -48,13 +54,15 @@ def _compile(src, verbose, build_dir, extra):
     return obj
 
 
-def build(verbose=False, out=OUT, src_dir=CSRC, build_dir=BUILD, extra_flags=()):
+def build(verbose=False, out=OUT, src_dir=CSRC, build_dir=BUILD, extra_flags=(), drop_flags=()):
     """Compile every source in ``src_dir`` and link ``out``. ``extra_flags`` are
-    appended to each compile (e.g. -D tile settings)."""
+    appended to each compile (e.g. -D tile settings); ``drop_flags`` lists flag
+    sequences removed from the defaults."""
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources(src_dir)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra_flags), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra_flags, drop_flags),
+                           srcs))
     tmp = out + ".tmp"
     # -z defs: an unresolved symbol (e.g. a kernel launch stub) fails the build
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs
