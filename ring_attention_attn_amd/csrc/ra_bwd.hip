@@ -396,12 +396,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
 //     keys of one KV head and walks the 64-row query tiles of every query head
 //     of the group. The waves come in pairs on the same 32 keys: the P wave
 //     computes S = Q K^T (K held as the MFMA B operand), P = exp(S - LSE) and
-//     dV^T += dO^T P; it hands P (bf16) to its partner through LDS, which one
-//     step later computes dP = dO V^T (V held), dS = P (dP - D) and
-//     dK^T += Q^T dS. Each wave keeps one accumulator set, so both fit two
-//     waves per SIMD, and no product is computed twice. Q and dO tiles reach
-//     LDS by DMA in an XOR-swizzled layout (three rotating buffers, one barrier
-//     per step), with the tile's LSE (log2 units) and D. Query rows are fed in
+//     dV^T += dO^T P, and hands P (bf16) to its partner through LDS; the
+//     partner (V held) computes dP = dO V^T of the same tile in the same step
+//     and, one step later, dS = P (dP - D) and dK^T += Q^T dS. Each wave keeps
+//     one accumulator set (the dK wave also one tile of dP), so both roles fit
+//     two waves per SIMD, and no product is computed twice. The dK wave
+//     starts each step with the dS products of the previous tile, the P wave
+//     with its score products, so their VALU-heavy phases do not coincide.
+//     Q tiles reach LDS by DMA two steps ahead (four rotating buffers), dO
+//     tiles one step ahead (two buffers), both XOR-swizzled, with the tile's
+//     LSE (log2 units) and D; one barrier per step. Query rows are fed in
 //     sigma order, so P and dS are directly B operands of the dV / dK
 //     products, whose A operands are read transposed from the same tiles.
 //     Each dK/dV element has one writer.
@@ -417,12 +421,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   __shared__ __attribute__((aligned(1024))) bf16_t sQ0[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sQ1[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sQ2[TB];
+  __shared__ __attribute__((aligned(1024))) bf16_t sQ3[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sG0[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sG1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sG2[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sP[2 * 4 * PB];  // two slots
-  __shared__ __attribute__((aligned(16))) float sL[3][QT];  // LSE * log2(e) (+inf: no contribution)
-  __shared__ __attribute__((aligned(16))) float sD[3][QT];
+  __shared__ __attribute__((aligned(16))) float sL[2][QT];  // LSE * log2(e) (+inf: no contribution)
+  __shared__ __attribute__((aligned(16))) float sD[4][QT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -479,55 +483,69 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   DmaSwz<QT, D, NW, 2> qst, gst;
   qst.init(p.q_ss, wave, lane);
   gst.init(p.do_ss, wave, lane);
+  // buffers by step position (compile-time, so DMA into one buffer never
+  // orders reads of another)
   auto qbuf = [&](auto b) -> bf16_t* {
-    constexpr int B = decltype(b)::value;
-    return B == 0 ? sQ0 : (B == 1 ? sQ1 : sQ2);
+    constexpr int B = decltype(b)::value & 3;
+    return B == 0 ? sQ0 : (B == 1 ? sQ1 : (B == 2 ? sQ2 : sQ3));
   };
   auto gbuf = [&](auto b) -> bf16_t* {
-    constexpr int B = decltype(b)::value;
-    return B == 0 ? sG0 : (B == 1 ? sG1 : sG2);
+    constexpr int B = decltype(b)::value & 1;
+    return B == 0 ? sG0 : sG1;
   };
-  // LSE and D of a tile: wave 0 loads them into registers when the tile's DMA
-  // is issued and writes them to LDS after its compute of that step
+  // (an invalid tile is still issued, with no rows in range, so that every
+  // step issues the same number of loads; it fills a free buffer with zeros)
+  auto stage_q = [&](int hh, int t, auto b, bool valid) {
+    const int h = g * p.group + (valid ? hh : 0);
+    const int64_t q0 = valid ? (int64_t)t * QT : 0;
+    qst.issue_untracked((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, q0, valid ? lq : q0,
+                        qbuf(b));
+  };
+  // dO of a tile with its LSE and D: wave 0 loads those into registers when
+  // the DMA is issued and writes them to LDS after its compute of that step
   float ld_l = INFINITY, ld_d = 0.f;
-  auto stage = [&](int hh, int t, auto b) {
+  auto stage_g = [&](int hh, int t, auto b) {
     const int h = g * p.group + hh;
     const int64_t q0 = (int64_t)t * QT;
-    qst.issue((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, q0, lq, qbuf(b));
-    gst.issue((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, q0, lq, gbuf(b));
+    gst.issue_untracked((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, q0, lq, gbuf(b));
     if (wave == 0) {
       const int64_t row = q0 + lane;
-      ld_l = INFINITY;
+      ld_l = -INFINITY;
       ld_d = 0.f;
       if (row < lq) {
-        const float l = p.lse_in[(int64_t)h * lq + row];
-        ld_l = l == -INFINITY ? INFINITY : l * kLog2e;  // empty row: no contribution
+        ld_l = p.lse_in[(int64_t)h * lq + row];
         ld_d = p.delta[(int64_t)h * lq + row];
       }
     }
   };
+  // (the loaded values are first used here, after the step's compute, so the
+  // loads do not stall it)
   auto store_ld = [&](auto b) {
     constexpr int B = decltype(b)::value;
     if (wave == 0) {
-      sL[B][lane] = ld_l;
-      sD[B][lane] = ld_d;
+      sL[B & 1][lane] = ld_l == -INFINITY ? INFINITY : ld_l * kLog2e;  // empty row: no contribution
+      sD[B & 3][lane] = ld_d;
     }
   };
 
   // per-lane byte offsets in a swizzled tile: 16-byte row reads of chunk
   // 2*c + hi of row qb*32 + sigma(l32), and transposing reads of rows
-  // 16*cq + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3)
-  int roff[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) roff[c] = swz_off<D>(srow, 2 * c + hi);
+  // 16*cq + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3).
+  // The swizzle is an XOR on the chunk index, so the offset for chunk c
+  // (block db) is that of chunk 0 (block 0) XOR 32*c (64*db); the bases are
+  // passed through an opaque copy every step, so the derived offsets are
+  // formed where they are used instead of being held across the loop.
   const int grp = lane >> 4, gi = lane & 15;
-  int toff[2][ND];
-#pragma unroll
-  for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-      toff[sh][db] = swz_off<D>(8 * hi + (gi >> 2) + 4 * sh, 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1)) +
-                     8 * (gi & 1);
+  const int roff_base = swz_off<D>(srow, hi);
+  const int toff_base0 = swz_off<D>(8 * hi + (gi >> 2), 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  const int toff_base1 = swz_off<D>(8 * hi + (gi >> 2) + 4, 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  int roff0 = roff_base, toff0 = toff_base0, toff1 = toff_base1;
+  auto refresh_offsets = [&]() {
+    roff0 = roff_base;
+    toff0 = toff_base0;
+    toff1 = toff_base1;
+    asm volatile("" : "+v"(roff0), "+v"(toff0), "+v"(toff1));
+  };
   // P hand-off slot of this lane: block (qb, hf) of key group kw, 16 bytes per lane
   const int p_lane = kw * PB + lane * 8;
 
@@ -539,7 +557,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
       x[qb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        x[qb] = mfma32(*(const bf16x8*)(tile + qb * 32 * 2 * D + roff[c]), breg[c], x[qb]);
+        x[qb] = mfma32(*(const bf16x8*)(tile + qb * 32 * 2 * D + (roff0 ^ (32 * c))), breg[c], x[qb]);
     }
   };
   // acc^T += tile^T B' over 16 query rows cq (B' = P or dS chunk in bf16)
@@ -547,22 +565,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const char* a = tile + 16 * cq * 2 * D;
-      const bf16x8 av = __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + toff[0][db])),
-                                                ds_read_tr((const bf16_t*)(a + toff[1][db])), 0,
+      const bf16x8 av = __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + (toff0 ^ (64 * db)))),
+                                                ds_read_tr((const bf16_t*)(a + (toff1 ^ (64 * db)))), 0,
                                                 1, 2, 3, 4, 5, 6, 7);
       acc[db] = mfma32(av, bv, acc[db]);
     }
   };
 
-
-  // P wave, tile `it` in buffer b: S, mask, P -> LDS slot ps, dV^T += dO^T P
-  auto p_step = [&](int t, auto b, int ps, auto mask_tag) {
-    constexpr int B = decltype(b)::value;
+  // P wave at step position I (tile i): S, mask, P -> LDS slot I % 2,
+  // dV^T += dO^T P
+  auto p_step = [&](int t, auto pos, auto mask_tag) {
+    constexpr int I = decltype(pos)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* cQ = (const char*)qbuf(b);
-    const char* cG = (const char*)gbuf(b);
-    f32x16 sacc[2];
-    row_products(cQ, sacc);
+    const char* cG = (const char*)gbuf(std::integral_constant<int, I>{});
+    f32x16 sc[2];
+    row_products((const char*)qbuf(std::integral_constant<int, I>{}), sc);
     if (MASK) {  // branch-free masking of the diagonal / ragged tiles
       const TileRows tq(p.qm, (int64_t)t * QT, QT);
       const QMaskBounds mb(tq, kpos, key_ok, 8 * hi, p.causal);
@@ -571,117 +588,145 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const bool vis = mb.row_visible(qb * 32 + 16 * (r >> 3) + (r & 7));
-          sacc[qb][r] = vis ? sacc[qb][r] : -INFINITY;
+          sc[qb][r] = vis ? sc[qb][r] : -INFINITY;
         }
     }
-    bf16_t* sp = sP + ps * 4 * PB + p_lane;
+    bf16_t* sp = sP + (I & 1) * 4 * PB + p_lane;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int qo = qb * 32 + 16 * hf + 8 * hi;
-        const f32x4 la = *(const f32x4*)(&sL[B][qo]), lb = *(const f32x4*)(&sL[B][qo + 4]);
+        const f32x4 la = *(const f32x4*)(&sL[I & 1][qo]), lb = *(const f32x4*)(&sL[I & 1][qo + 4]);
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float l2 = e < 4 ? la[e] : lb[e - 4];
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * hf + e], p.scale_log2, -l2));
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[qb][8 * hf + e], p.scale_log2, -l2));
         }
         const bf16x8 pk = pack_bf16x8(pv);
         *(bf16x8*)(sp + (2 * qb + hf) * 512) = pk;
         col_products(cG, 2 * qb + hf, pk);
       }
   };
-  // dK wave, tile `it` in buffer b with its P in slot ps: dP, dS, dK^T += Q^T dS
-  auto k_step = [&](auto b, int ps) {
-    constexpr int B = decltype(b)::value;
-    const char* cQ = (const char*)qbuf(b);
-    const char* cG = (const char*)gbuf(b);
-    f32x16 pacc[2];
-    row_products(cG, pacc);
-    const bf16_t* sp = sP + ps * 4 * PB + p_lane;
+  // dK wave at step position I: dS of tile i - 1 (its dP in dp, its P in
+  // slot (I - 1) % 2), dK^T += Q^T dS, then dP of tile i into dp
+  // (unconditionally: past the last tile it is discarded). The dS products
+  // come first, so the pair's VALU-heavy phases (softmax here, dS there) fall
+  // against the other wave's matrix products.
+  f32x16 dp[2];
+  auto k_step = [&](auto pos, auto ds_tag) {
+    constexpr int I = decltype(pos)::value;
+    constexpr bool DS = decltype(ds_tag)::value;
+    if (DS) {
+      const char* cQ = (const char*)qbuf(std::integral_constant<int, I + 3>{});
+      const bf16_t* sp = sP + ((I + 1) & 1) * 4 * PB + p_lane;
+      constexpr int DSL = (I + 3) & 3;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int qo = qb * 32 + 16 * hf + 8 * hi;
-        const f32x4 da = *(const f32x4*)(&sD[B][qo]), db_ = *(const f32x4*)(&sD[B][qo + 4]);
-        const bf16x8 pk = *(const bf16x8*)(sp + (2 * qb + hf) * 512);
-        float sv[8];
+        for (int hf = 0; hf < 2; ++hf) {
+          const int qo = qb * 32 + 16 * hf + 8 * hi;
+          const f32x4 da = *(const f32x4*)(&sD[DSL][qo]), db_ = *(const f32x4*)(&sD[DSL][qo + 4]);
+          const bf16x8 pk = *(const bf16x8*)(sp + (2 * qb + hf) * 512);
+          float sv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float dl = e < 4 ? da[e] : db_[e - 4];
-          sv[e] = (float)pk[e] * (pacc[qb][8 * hf + e] - dl);
+          for (int e = 0; e < 8; ++e) {
+            const float dl = e < 4 ? da[e] : db_[e - 4];
+            sv[e] = (float)pk[e] * (dp[qb][8 * hf + e] - dl);
+          }
+          col_products(cQ, 2 * qb + hf, pack_bf16x8(sv));
         }
-        col_products(cQ, 2 * qb + hf, pack_bf16x8(sv));
-      }
+    }
+    row_products((const char*)gbuf(std::integral_constant<int, I>{}), dp);
   };
 
-  // Step i: tile i is in buffer i % 3, tile i - 1 in buffer (i - 1) % 3; the
-  // DMA of tile i + 1 goes to buffer (i + 1) % 3 (last read at step i - 2).
-  // P waves compute tile i (P into slot i % 2); dK waves compute tile i - 1.
-  // The two roles run separate loops with the same barrier sequence, so each
-  // role's registers are allocated on their own.
+  // Step i (position I = i % 4): Q and dO of tile i have landed at this
+  // step's barrier (Q of tile i + 1 may still be in flight); the DMA of dO of
+  // tile i + 1 goes to the dO buffer read by both roles one step ago, then
+  // that of Q of tile i + 2 to the Q buffer last read by the dK waves one step
+  // ago. The two roles run
+  // separate loops with the same barrier sequence, so each role's registers
+  // are allocated on their own.
   int ch = t_first < qt_wg.n ? 0 : p.group, ct = t_first;  // tile i
-  int slot = 0;                                            // P slot of tile i
+  int nh = ch, nt = ct;                                    // tile i + 1
+  if (ch < p.group) advance(nh, nt);
   bool have_prev = false;
-  auto step = [&](auto bc, auto bp, auto bn, auto role) {
+  // The Q DMA of the previous step is the last vector-memory operation issued
+  // and is read no earlier than the next step: the waits leave it in flight.
+  constexpr int QDMA = DmaSwz<QT, D, NW, 2>::PER;  // DMA instructions per lane per tile
+  static_assert((QT * 2 * D / 1024) % NW == 0, "every wave issues QDMA loads per tile");
+  auto step = [&](auto pos, auto role) {
+    constexpr int I = decltype(pos)::value;
     constexpr bool PW = decltype(role)::value;
-    wait_vmem();
-    __syncthreads();  // tile i visible (with LSE/D); P of tile i-1 visible; buffer bn free
+    wait_vmem_n<QDMA>();
+    barrier_lds();  // Q(i), dO(i), LSE(i), D(i-1), P(i-1) visible; DMA targets free
+    refresh_offsets();
     const bool cur = ch < p.group;
-    int nh = ch, nt = ct;
-    if (cur) advance(nh, nt);
     const bool nxt = nh < p.group;
-    if (nxt) stage(nh, nt, bn);
+    int n2h = nh, n2t = nt;
+    if (nxt) advance(n2h, n2t);
+    if (nxt) stage_g(nh, nt, std::integral_constant<int, I + 1>{});
+    asm volatile("" ::: "memory");  // keep the Q DMA last
+    stage_q(n2h, n2t, std::integral_constant<int, I + 2>{}, n2h < p.group);
     if (wave_has_keys) {
       if (PW) {
         if (cur) {
           if (qt_w.mask_free(ct))
-            p_step(ct, bc, slot, std::false_type{});
+            p_step(ct, pos, std::false_type{});
           else
-            p_step(ct, bc, slot, std::true_type{});
+            p_step(ct, pos, std::true_type{});
         }
-      } else if (have_prev) {
-        k_step(bp, slot ^ 1);
+      } else {
+        if (have_prev)
+          k_step(pos, std::true_type{});
+        else
+          k_step(pos, std::false_type{});
       }
     }
-    if (nxt) store_ld(bn);  // becomes visible at the next step's barrier
+    if (nxt) store_ld(std::integral_constant<int, I + 1>{});  // visible at the next barrier
     have_prev = cur;
     ch = nh;
     ct = nt;
-    slot ^= 1;
+    nh = n2h;
+    nt = n2t;
     return have_prev;
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
   if (ch < p.group) {
-    stage(ch, ct, B0{});
-    store_ld(B0{});
-    // three-step unroll: buffer indices are compile-time constants
+    stage_q(ch, ct, P0{}, true);
+    stage_q(nh, nt, P1{}, nh < p.group);
+    stage_g(ch, ct, P0{});
+    store_ld(P0{});
+    wait_vmem();
+    __syncthreads();
+    // four-step unroll: buffer indices are compile-time constants
     if (pwave) {
       const std::true_type r{};
-      while (step(B0{}, B2{}, B1{}, r) && step(B1{}, B0{}, B2{}, r) && step(B2{}, B1{}, B0{}, r)) {
+      while (step(P0{}, r) && step(P1{}, r) && step(P2{}, r) && step(P3{}, r)) {
       }
     } else {
       const std::false_type r{};
-      while (step(B0{}, B2{}, B1{}, r) && step(B1{}, B0{}, B2{}, r) && step(B2{}, B1{}, B0{}, r)) {
+      while (step(P0{}, r) && step(P1{}, r) && step(P2{}, r) && step(P3{}, r)) {
       }
     }
+    wait_vmem();  // the last (empty) Q DMA lands before the workgroup's LDS is released
   }
 
   // ---- epilogue: lanes = keys, registers = d rows 8*(r/4) + 4*hi + r%4
   if (!key_ok) return;
   float* dst = (pwave ? p.dv : p.dk) + mykey * p.dk_ss + (int64_t)g * p.dk_hs;
-  const float sc = pwave ? 1.f : p.scale;
+  const float out_scale = pwave ? 1.f : p.scale;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4 a;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = acc[db][4 * i + j] * sc;
+      for (int j = 0; j < 4; ++j) a[j] = acc[db][4 * i + j] * out_scale;
       f32x4* pa = (f32x4*)(dst + 32 * db + 8 * i + 4 * hi);
       if (p.dkv_accumulate) a += *pa;
       *pa = a;

@@ -252,7 +252,31 @@ struct DmaSwz {
                                                  voff[k], 0, 0, 0);
     }
   }
+  // Same, with the LDS destination passed as an opaque address: the compiler
+  // then does not tie later LDS reads to these loads (it would otherwise wait
+  // for them before reading a buffer it cannot tell apart from the target).
+  // The caller orders every read of the target after an explicit vmcnt wait.
+  __device__ __forceinline__ void issue_untracked(const bf16_t* base, int64_t ss, int64_t row0,
+                                                  int64_t nrows, bf16_t* lds) const {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+    uint32_t a = (uint32_t)(uintptr_t)(lds_void*)lds;
+    asm volatile("" : "+s"(a));
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = wave + k * NW;
+      if (j < NJ)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)(a + 1024 * j), 16,
+                                                 voff[k], 0, 0, 0);
+    }
+  }
 };
+
+// Workgroup barrier ordering LDS only: waits for this wave's LDS operations
+// but, unlike __syncthreads(), not for its outstanding vector-memory loads
+// (LDS-DMA included); the memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Wait until this wave's outstanding vector-memory operations (LDS-DMA loads
 // included) are complete.
@@ -294,6 +318,14 @@ struct TilePos {
   }
 };
 
+// x ? a : b on values. (A conditional over two struct members is an lvalue
+// select, which can leave the struct in scratch memory.)
+__device__ __forceinline__ int sel_int(bool x, int a, int b) { return x ? a : b; }
+// int64 -> int32, saturating
+__device__ __forceinline__ int sat_int(int64_t x) {
+  return x > INT_MAX ? INT_MAX : (x < INT_MIN ? INT_MIN : (int)x);
+}
+
 // int32 positions of the rows [t0, t0 + n) of a SegMap, for branch-free
 // masking: row t0 + off is at pos(off) while off < split (first run), and
 // rows at or past nvalid do not exist. All fields are wave-uniform.
@@ -307,7 +339,7 @@ struct TileRows {
     const int64_t v = m.len - t0;
     nvalid = v < 0 ? 0 : (v > n ? n : (int)v);
   }
-  __device__ __forceinline__ int pos(int off) const { return (off < split ? base0 : base1) + off; }
+  __device__ __forceinline__ int pos(int off) const { return sel_int(off < split, base0, base1) + off; }
 };
 
 // Rows of a SegMap whose position is <= x: [0, c0) of the first run and
@@ -370,17 +402,12 @@ struct MaskBounds {
   __device__ __forceinline__ MaskBounds(const TileRows& t, int qlim, int u, int causal) {
     nv = t.nvalid - u;
     sp = t.split - u;
-    if (causal) {
-      // qlim - base - u, saturated to the int32 range
-      const int64_t x0 = (int64_t)qlim - t.base0 - u, x1 = (int64_t)qlim - t.base1 - u;
-      a0 = x0 > INT_MAX ? INT_MAX : (x0 < INT_MIN ? INT_MIN : (int)x0);
-      a1 = x1 > INT_MAX ? INT_MAX : (x1 < INT_MIN ? INT_MIN : (int)x1);
-    } else {
-      a0 = a1 = INT_MAX;
-    }
+    // qlim - base - u, saturated to the int32 range
+    a0 = causal ? sat_int((int64_t)qlim - t.base0 - u) : INT_MAX;
+    a1 = causal ? sat_int((int64_t)qlim - t.base1 - u) : INT_MAX;
   }
   __device__ __forceinline__ bool key_visible(int c) const {
-    return (c < nv) & (c <= (c < sp ? a0 : a1));
+    return (c < nv) & (c <= sel_int(c < sp, a0, a1));
   }
 };
 
@@ -443,18 +470,15 @@ struct QMaskBounds {
                                          int causal) {
     nv = t.nvalid - u;
     sp = t.split - u;
-    if (!key_ok) {
-      a0 = a1 = INT_MAX;
-    } else if (causal) {
-      const int64_t x0 = (int64_t)kpos - t.base0 - u, x1 = (int64_t)kpos - t.base1 - u;
-      a0 = x0 > INT_MAX ? INT_MAX : (x0 < INT_MIN ? INT_MIN : (int)x0);
-      a1 = x1 > INT_MAX ? INT_MAX : (x1 < INT_MIN ? INT_MIN : (int)x1);
-    } else {
-      a0 = a1 = INT_MIN;
-    }
+    // kpos - base - u, saturated to the int32 range (selects, no branches:
+    // key_ok differs between lanes)
+    const int c0 = causal ? sat_int((int64_t)kpos - t.base0 - u) : INT_MIN;
+    const int c1 = causal ? sat_int((int64_t)kpos - t.base1 - u) : INT_MIN;
+    a0 = sel_int(key_ok, c0, INT_MAX);
+    a1 = sel_int(key_ok, c1, INT_MAX);
   }
   __device__ __forceinline__ bool row_visible(int c) const {
-    return (c < nv) & (c >= (c < sp ? a0 : a1));
+    return (c < nv) & (c >= sel_int(c < sp, a0, a1));
   }
 };
 
