@@ -392,6 +392,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     }
 }
 
+// dK/dV kernel tuning: LDS reads issued ahead of the score products, and the
+// wave priority of the P waves (whose chain sets the step time)
+#ifndef RA_DKV_AHEAD
+#define RA_DKV_AHEAD 8
+#endif
+#ifndef RA_DKV_PPRIO
+#define RA_DKV_PPRIO 1
+#endif
+
 // (2) dK, dV, key-stationary: a workgroup of 8 waves (two per SIMD) owns 128
 //     keys of one KV head and walks the 64-row query tiles of every query head
 //     of the group. The waves come in pairs on the same 32 keys: the P wave
@@ -501,30 +510,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     qst.issue_untracked((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, q0, valid ? lq : q0,
                         qbuf(b));
   };
-  // dO of a tile with its LSE and D: wave 0 loads those into registers when
-  // the DMA is issued and writes them to LDS after its compute of that step
-  float ld_l = INFINITY, ld_d = 0.f;
   auto stage_g = [&](int hh, int t, auto b) {
     const int h = g * p.group + hh;
-    const int64_t q0 = (int64_t)t * QT;
-    gst.issue_untracked((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, q0, lq, gbuf(b));
+    gst.issue_untracked((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, (int64_t)t * QT, lq,
+                        gbuf(b));
+  };
+  // LSE and D of a tile: wave 0 loads them into registers two steps before the
+  // tile is used and writes them to LDS at the end of the next step, so the
+  // loads never stall a step
+  float pl = -INFINITY, pd = 0.f;  // loaded one step ago
+  float nl = -INFINITY, nd = 0.f;  // loaded in this step
+  auto load_ld = [&](int hh, int t, float& l, float& d) {
     if (wave == 0) {
-      const int64_t row = q0 + lane;
-      ld_l = -INFINITY;
-      ld_d = 0.f;
+      const int h = g * p.group + hh;
+      const int64_t row = (int64_t)t * QT + lane;
+      l = -INFINITY;
+      d = 0.f;
       if (row < lq) {
-        ld_l = p.lse_in[(int64_t)h * lq + row];
-        ld_d = p.delta[(int64_t)h * lq + row];
+        l = p.lse_in[(int64_t)h * lq + row];
+        d = p.delta[(int64_t)h * lq + row];
       }
     }
   };
-  // (the loaded values are first used here, after the step's compute, so the
-  // loads do not stall it)
-  auto store_ld = [&](auto b) {
+  auto store_ld = [&](auto b, float l, float d) {
     constexpr int B = decltype(b)::value;
     if (wave == 0) {
-      sL[B & 1][lane] = ld_l == -INFINITY ? INFINITY : ld_l * kLog2e;  // empty row: no contribution
-      sD[B & 3][lane] = ld_d;
+      sL[B & 1][lane] = l == -INFINITY ? INFINITY : l * kLog2e;  // empty row: no contribution
+      sD[B & 3][lane] = d;
     }
   };
 
@@ -572,15 +584,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     }
   };
 
+  // score block: S = Q K^T of the tile in buffer b into sc, with the tile
+  // reads issued AH products ahead
+  f32x16 sc[2];
+  auto scores = [&](auto b) {
+    row_products((const char*)qbuf(b), sc);
+    constexpr int AH = RA_DKV_AHEAD < 2 * NC ? RA_DKV_AHEAD : 2 * NC;
+    if (AH > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < 2 * NC - AH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+    }
+  };
   // P wave at step position I (tile i): S, mask, P -> LDS slot I % 2,
   // dV^T += dO^T P
-  auto p_step = [&](int t, auto pos, auto mask_tag) {
+  auto p_step = [&](int t, auto pos) {
     constexpr int I = decltype(pos)::value;
-    constexpr bool MASK = decltype(mask_tag)::value;
     const char* cG = (const char*)gbuf(std::integral_constant<int, I>{});
-    f32x16 sc[2];
-    row_products((const char*)qbuf(std::integral_constant<int, I>{}), sc);
-    if (MASK) {  // branch-free masking of the diagonal / ragged tiles
+    scores(std::integral_constant<int, I>{});
+    // masking of the diagonal / ragged tiles: a uniform branch around
+    // branch-free selects that rewrite the scores in place (a whole second copy
+    // of the step would keep the accumulators in other registers and copy them
+    // back at the join)
+    if (!qt_w.mask_free(t)) {
       const TileRows tq(p.qm, (int64_t)t * QT, QT);
       const QMaskBounds mb(tq, kpos, key_ok, 8 * hi, p.causal);
 #pragma unroll
@@ -667,16 +697,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     int n2h = nh, n2t = nt;
     if (nxt) advance(n2h, n2t);
     if (nxt) stage_g(nh, nt, std::integral_constant<int, I + 1>{});
+    if (n2h < p.group) load_ld(n2h, n2t, nl, nd);
     asm volatile("" ::: "memory");  // keep the Q DMA last
     stage_q(n2h, n2t, std::integral_constant<int, I + 2>{}, n2h < p.group);
     if (wave_has_keys) {
       if (PW) {
-        if (cur) {
-          if (qt_w.mask_free(ct))
-            p_step(ct, pos, std::false_type{});
-          else
-            p_step(ct, pos, std::true_type{});
-        }
+        if (cur) p_step(ct, pos);
       } else {
         if (have_prev)
           k_step(pos, std::true_type{});
@@ -684,7 +710,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
           k_step(pos, std::false_type{});
       }
     }
-    if (nxt) store_ld(std::integral_constant<int, I + 1>{});  // visible at the next barrier
+    if (nxt) store_ld(std::integral_constant<int, I + 1>{}, pl, pd);  // visible at the next barrier
+    pl = nl;
+    pd = nd;
     have_prev = cur;
     ch = nh;
     ct = nt;
@@ -700,12 +728,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     stage_q(ch, ct, P0{}, true);
     stage_q(nh, nt, P1{}, nh < p.group);
     stage_g(ch, ct, P0{});
-    store_ld(P0{});
+    load_ld(ch, ct, pl, pd);
+    store_ld(P0{}, pl, pd);
+    if (nh < p.group) load_ld(nh, nt, pl, pd);
     wait_vmem();
     __syncthreads();
     // four-step unroll: buffer indices are compile-time constants
     if (pwave) {
       const std::true_type r{};
+      if (RA_DKV_PPRIO) __builtin_amdgcn_s_setprio(RA_DKV_PPRIO);
       while (step(P0{}, r) && step(P1{}, r) && step(P2{}, r) && step(P3{}, r)) {
       }
     } else {
