@@ -3,7 +3,9 @@
 fwd + bwd, on MI355X.
 
 A step is one pass of the whole path over the share: P forward ring steps with
-log-sum-exp merges, the backward preprocess, and P backward ring steps, on
+log-sum-exp merges (fused into the forward kernel's epilogue by default;
+--merge separate runs lse_merge as its own kernel), the backward preprocess, and
+P backward ring steps, on
 seeded synthetic inputs already resident in HBM. The default workload is the
 LLaMA-3-8B-shaped share at context degree 8 (32 Q / 8 KV heads, d = 128, bf16,
 global sequence 131,072 tokens, local 16,384 rows as two paired blocks of 8,192).
@@ -120,6 +122,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0, help="ring rank whose share is timed")
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--merge", choices=("fused", "separate"), default="fused",
+                    help="fold each forward step into the running result in the forward "
+                         "kernel (fused) or with a separate lse_merge launch")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one head_permute of 1 GiB (a plain copy of known size) before the "
                          "warmup, to calibrate HBM byte counters")
@@ -141,7 +146,8 @@ def main():
     log(f"config {cfg.name}: S={cfg.S} P={cfg.P} ({cfg.inner}x{cfg.outer}) hq={cfg.hq} "
         f"hkv={cfg.hkv} d={cfg.d} {cfg.dtype} rank={args.rank}")
     q, K, V, do = make_inputs(cfg, args.rank)
-    ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d, cfg.dtype)
+    ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d, cfg.dtype,
+                     merge=args.merge)
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(7)   # 1 GiB
         dst = torch.empty_like(src)
@@ -164,12 +170,16 @@ def main():
     def timed_step():
         for t, (j, desc) in enumerate(ring.descs):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            o, l = (ring.o_acc, ring.lse_acc) if t == 0 else (ring.o_step, ring.lse_step)
+            fused = t > 0 and args.merge == "fused"
+            o, l = (ring.o_acc, ring.lse_acc) if t == 0 or fused else (ring.o_step, ring.lse_step)
             e0.record(stream)
-            B.ring_attn_step_fwd(desc, q, K[j], V[j], o, l)
+            if fused:
+                B.ring_attn_step_fwd_merge(desc, q, K[j], V[j], o, l)
+            else:
+                B.ring_attn_step_fwd(desc, q, K[j], V[j], o, l)
             e1.record(stream)
             ev["fwd"].append((e0, e1))
-            if t > 0:
+            if t > 0 and not fused:
                 m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 m0.record(stream)
                 B.lse_merge(ring.L, ring.hq, ring.d, ring.o_acc, ring.lse_acc, ring.o_step,
@@ -203,6 +213,20 @@ def main():
     def avg_ms(pairs):
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
 
+    if args.merge == "fused":
+        # the merge runs inside the forward launches; time the standalone kernel
+        # (outside the timed steps) for its own bandwidth figure
+        ring.o_step.zero_()
+        ring.lse_step.zero_()
+        for _ in range(6):
+            m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            m0.record(stream)
+            B.lse_merge(ring.L, ring.hq, ring.d, ring.o_acc, ring.lse_acc, ring.o_step,
+                        ring.lse_step)
+            m1.record(stream)
+            ev["merge"].append((m0, m1))
+        torch.cuda.synchronize()
+        ev["merge"] = ev["merge"][1:]
     fwd_ms, bwd_ms, merge_ms = avg_ms(ev["fwd"]), avg_ms(ev["bwd"]), avg_ms(ev["merge"])
     # algorithmic flops per launch: each ring step carries 1/P of the share's pairs
     # (2b^2 per head per step, +b on the diagonal step); averaged over the P launches
@@ -228,6 +252,7 @@ def main():
                    "local_rows": cfg.rows, "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.d,
                    "rank": args.rank, "parallelism": "one GPU's share (virtual ring)"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "merge": args.merge,
         "breakdown_ms_per_launch": {"step_fwd": round(fwd_ms, 4), "step_bwd": round(bwd_ms, 4),
                                     "lse_merge": round(merge_ms, 4)},
         "step_fwd_tflops": round(fwd_tflops, 1),

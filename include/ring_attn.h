@@ -104,6 +104,22 @@ ra_status ring_attn_step_fwd(const ra_step_desc* desc, const void* q, const void
                              ra_stream_t stream);
 
 /*
+ * ring_attn_step_fwd_merge -- ring_attn_step_fwd followed by lse_merge of its
+ * result into the running (o_acc, lse_acc), in one kernel: the step's rows are
+ * folded into the accumulators in the kernel's epilogue (the merge formula of
+ * lse_merge, below) and never written out, which saves the step's O_step and
+ * LSE_step round trip through memory.
+ * o_acc: fp32 with desc's o strides; lse_acc: fp32 [hq][lq]; both updated in
+ * place (initialise them as for lse_merge: lse_acc = -inf, o_acc = 0, or with a
+ * first step). A row with no visible key in this chunk is left unchanged; an
+ * empty chunk (lk == 0) launches nothing. Same inputs, arithmetic and errors as
+ * ring_attn_step_fwd; calls that overlap on the same accumulators race.
+ */
+ra_status ring_attn_step_fwd_merge(const ra_step_desc* desc, const void* q, const void* k,
+                                   const void* v, float* o_acc, float* lse_acc,
+                                   ra_stream_t stream);
+
+/*
  * ring_attn_step_bwd -- one step's share of the attention gradient, driven by
  * the FINAL log-sum-exp and D of the rows (saved-LSE recompute).
  *

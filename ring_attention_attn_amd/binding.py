@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EALIGN, RA_EDEVICE = 0, 1, 2, 3, 4
 RA_BF16, RA_F32 = 0, 1
 
-EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_bwd", "lse_merge", "ra_bwd_delta",
+EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_fwd_merge", "ring_attn_step_bwd", "lse_merge",
+           "ra_bwd_delta",
            "head_permute", "ra_fill_f32", "ra_zigzag_positions", "ra_zigzag_segments",
            "ra_double_ring_order", "ra_validate_step", "ra_status_str")
 
@@ -62,6 +63,7 @@ def lib():
         pd = ctypes.POINTER(RaStepDesc)
         sig = {
             "ring_attn_step_fwd": [pd, vp, vp, vp, vp, vp, vp],
+            "ring_attn_step_fwd_merge": [pd, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_bwd": [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "lse_merge": [i64, i32, i32, vp, vp, vp, vp, vp],
             "ra_bwd_delta": [i64, i32, i32, i32, vp, vp, vp, vp, vp],
@@ -115,6 +117,12 @@ def _stream(stream):
 def ring_attn_step_fwd(desc, q, k, v, o_step, lse_step, stream=None):
     _check(lib().ring_attn_step_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o_step),
                                     _ptr(lse_step), _stream(stream)), "ring_attn_step_fwd")
+
+
+def ring_attn_step_fwd_merge(desc, q, k, v, o_acc, lse_acc, stream=None):
+    _check(lib().ring_attn_step_fwd_merge(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(o_acc), _ptr(lse_acc), _stream(stream)),
+           "ring_attn_step_fwd_merge")
 
 
 def ring_attn_step_bwd(desc, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, stream=None):

@@ -122,6 +122,23 @@ ra_status ring_attn_step_fwd(const ra_step_desc* d, const void* q, const void* k
   return from_hip(launch_step_fwd(p, d->dtype, d->head_dim, (hipStream_t)stream));
 }
 
+ra_status ring_attn_step_fwd_merge(const ra_step_desc* d, const void* q, const void* k,
+                                   const void* v, float* o_acc, float* lse_acc,
+                                   ra_stream_t stream) {
+  ra_status st = ra_validate_step(d, 0);
+  if (st != RA_OK) return st;
+  const int64_t lq = (int64_t)d->q_nseg * d->q_seg_len;
+  const int64_t lk = (int64_t)d->k_nseg * d->k_seg_len;
+  if (lq == 0 || lk == 0) return RA_OK;  // an empty chunk leaves the accumulators as they are
+  if (!q || !k || !v || !o_acc || !lse_acc) return RA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_acc) || !aligned16(lse_acc))
+    return RA_EALIGN;
+  StepParams p = make_params(d);
+  p.q = q; p.k = k; p.v = v; p.o = o_acc; p.lse_out = lse_acc;
+  p.merge = 1;
+  return from_hip(launch_step_fwd(p, d->dtype, d->head_dim, (hipStream_t)stream));
+}
+
 ra_status ring_attn_step_bwd(const ra_step_desc* d, const void* q, const void* k, const void* v,
                              const void* dout, const float* lse, const float* delta,
                              float* dq_acc, float* dk_acc, float* dv_acc, ra_stream_t stream) {

@@ -42,9 +42,30 @@ constexpr float kLn2 = 0.69314718055994531f;
 __device__ inline float to_f(bf16_t x) { return (float)x; }
 __device__ inline float to_f(float x) { return x; }
 
+// Fold a step's row (O_s, L_s) into the running (O_a, L_a), as the merge of
+// partial results over disjoint key sets does: m = max(La, Ls);
+// L = m + ln(e^(La-m) + e^(Ls-m)), O = ca Oa + cs Os with ca = e^(La-L),
+// cs = e^(Ls-L). A step row with no visible key (Ls = -inf) leaves the row as
+// it is, so `update` is false and nothing is read or written for it.
+struct MergeCoeffs {
+  bool update;
+  float ca, cs, lse;
+};
+__device__ inline MergeCoeffs merge_coeffs(float la, float ls) {
+  MergeCoeffs r;
+  r.update = ls != -INFINITY;
+  const float m = fmaxf(la, ls);
+  const float ea = r.update ? expf(la - m) : 1.f, es = r.update ? expf(ls - m) : 0.f;
+  const float tot = ea + es, inv = 1.0f / tot;
+  r.ca = ea * inv;
+  r.cs = es * inv;
+  r.lse = r.update ? m + logf(tot) : la;
+  return r;
+}
+
 // ============================================================= VALU kernel
 // TPR lanes per query row (D/64), each holding 64 of the d components.
-template <int D, typename T>
+template <int D, typename T, bool MERGE>
 __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
   constexpr int TPR = D / 64;
   constexpr int RPB = 64 / TPR;  // rows per block
@@ -106,9 +127,22 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
   }
   if (!valid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float ls = l > 0.f ? m + logf(l) : -INFINITY;
+  float* orow = p.o + row * p.o_ss + h * p.o_hs + sub * 64;
+  float* lrow = p.lse_out + (int64_t)h * p.qm.len + row;
+  if (MERGE) {
+    // both lanes of the row read L_a before one of them writes it back
+    const MergeCoeffs mc = merge_coeffs(*lrow, ls);
+    if (mc.update) {
 #pragma unroll
-  for (int x = 0; x < 64; ++x) p.o[row * p.o_ss + h * p.o_hs + sub * 64 + x] = o[x] * inv;
-  if (sub == 0) p.lse_out[(int64_t)h * p.qm.len + row] = l > 0.f ? m + logf(l) : -INFINITY;
+      for (int x = 0; x < 64; ++x) orow[x] = mc.ca * orow[x] + mc.cs * (o[x] * inv);
+      if (sub == 0) *lrow = mc.lse;
+    }
+    return;
+  }
+#pragma unroll
+  for (int x = 0; x < 64; ++x) orow[x] = o[x] * inv;
+  if (sub == 0) *lrow = ls;
 }
 
 // ============================================================= MFMA kernel
@@ -120,7 +154,7 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 // each wave. Tiles use the XOR-swizzled row layout: K rows are read with
 // 16-byte loads and V^T operands with ds_read_b64_tr_b16, both free of bank
 // conflicts. Diagonal tiles and ragged tails add one branch-free masking block.
-template <int D>
+template <int D, bool MERGE>
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
                                                           int rows_per_wg) {
   constexpr int NW = 8;            // waves per workgroup
@@ -202,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   const int n_kt = kt_wg.n;
   auto next_visible = [&](int t) { return kt_wg.next(t); };
 
-  DmaSwz<KT, D, NW, 0> kst, vst;
+  DmaSwz<KT, D, NW, MERGE ? 5 : 0> kst, vst;
   kst.init(p.k_ss, wave, lane);
   vst.init(p.v_ss, wave, lane);
   auto kbuf = [&](auto b) -> bf16_t* {
@@ -389,23 +423,43 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     }
   }
 
-  // ---- epilogue: normalise, write O_step [row][h][d] and LSE_step [h][row]
+  // ---- epilogue: normalise, write O_step [row][h][d] and LSE_step [h][row],
+  // or fold them into O_acc and LSE_acc
   if (!wave_active) return;
   const float ltot = sum_halves(l_run);
   if (qok) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float ls = ltot > 0.f ? (m_run + log2f(ltot)) * kLn2 : -INFINITY;
     float* orow = p.o + qrow * p.o_ss + (int64_t)h * p.o_hs;
+    float* lrow = p.lse_out + (int64_t)h * lq + qrow;
+    if (MERGE) {
+      // both lane halves read L_a before one of them writes it back
+      const MergeCoeffs mc = merge_coeffs(*lrow, ls);
+      if (mc.update) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v4;
+          for (int i = 0; i < 4; ++i) {
+            f32x4* pa = (f32x4*)(orow + 32 * db + 8 * i + 4 * hi);
+            f32x4 a = *pa;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = oacc[db][4 * i + j] * inv;
-        *(f32x4*)(orow + 32 * db + 8 * i + 4 * hi) = v4;
+            for (int j = 0; j < 4; ++j) a[j] = mc.ca * a[j] + mc.cs * (oacc[db][4 * i + j] * inv);
+            *pa = a;
+          }
+        if (hi == 0) *lrow = mc.lse;
       }
-    if (hi == 0)
-      p.lse_out[(int64_t)h * lq + qrow] = ltot > 0.f ? (m_run + log2f(ltot)) * kLn2 : -INFINITY;
+    } else {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 v4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = oacc[db][4 * i + j] * inv;
+          *(f32x4*)(orow + 32 * db + 8 * i + 4 * hi) = v4;
+        }
+      if (hi == 0) *lrow = ls;
+    }
   }
 }
 
@@ -425,8 +479,12 @@ hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
   const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw, n_qt,
-                     rows_per_wg);
+  if (p.merge)
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw,
+                       n_qt, rows_per_wg);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, false>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw,
+                       n_qt, rows_per_wg);
   return hipGetLastError();
 }
 
@@ -434,7 +492,10 @@ template <int D, typename T>
 hipError_t launch_simple(const StepParams& p, hipStream_t s) {
   constexpr int RPB = 64 / (D / 64);
   const unsigned gx = (unsigned)((p.qm.len + RPB - 1) / RPB);
-  hipLaunchKernelGGL((fwd_simple_kernel<D, T>), dim3(gx, p.hq), dim3(64), 0, s, p);
+  if (p.merge)
+    hipLaunchKernelGGL((fwd_simple_kernel<D, T, true>), dim3(gx, p.hq), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_simple_kernel<D, T, false>), dim3(gx, p.hq), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct StepParams {
   int32_t hq, hkv, group;  // group = hq / hkv
   int32_t causal;
   int32_t dkv_accumulate;
+  int32_t merge;           // fwd: fold the step into (o, lse_out) = (O_acc, LSE_acc)
   float scale;             // softmax scale
   float scale_log2;        // scale * log2(e)
 };

@@ -5,9 +5,10 @@ On one device the ring is a loop over the KV chunks (all resident in HBM) in
 the double-ring visit order, where a multi-GPU ring would receive chunk j from
 its predecessor at step t ("Guide to LoongTrain", "The Communication Overhead
 and Causal Imbalance of Ring Attention"; "3. Double-Ring Asynchronous
-Communication Pipeline"). Forward: for each step, ring_attn_step_fwd then
-lse_merge into the running (O, LSE) -- the first step writes the running
-result directly. Backward: ra_bwd_delta (D = rowsum(dO O) and O in bf16), dq
+Communication Pipeline"). Forward: the first step writes the running (O, LSE)
+directly; every later step is folded into it, either by the fused
+ring_attn_step_fwd_merge (default) or by ring_attn_step_fwd then lse_merge
+(merge="separate"). Backward: ra_bwd_delta (D = rowsum(dO O) and O in bf16), dq
 cleared with ra_fill_f32, then ring_attn_step_bwd per step with the final LSE.
 
 PyTorch only allocates device memory and provides the stream.
@@ -28,7 +29,10 @@ class ShareRing:
     """
 
     def __init__(self, S, inner, outer, rank, hq, hkv, d, dtype="bf16", scale=None,
-                 device="cuda", causal=1):
+                 device="cuda", causal=1, merge="fused"):
+        if merge not in ("fused", "separate"):
+            raise ValueError(f"merge must be 'fused' or 'separate', not {merge!r}")
+        self.merge = merge
         self.S, self.inner, self.outer, self.rank = S, inner, outer, rank
         self.P = inner * outer
         self.hq, self.hkv, self.d, self.dtype = hq, hkv, d, dtype
@@ -62,6 +66,8 @@ class ShareRing:
         for t, (j, desc) in enumerate(self.descs):
             if t == 0:
                 B.ring_attn_step_fwd(desc, q, K[j], V[j], self.o_acc, self.lse_acc, stream)
+            elif self.merge == "fused":
+                B.ring_attn_step_fwd_merge(desc, q, K[j], V[j], self.o_acc, self.lse_acc, stream)
             else:
                 B.ring_attn_step_fwd(desc, q, K[j], V[j], self.o_step, self.lse_step, stream)
                 B.lse_merge(self.L, self.hq, self.d, self.o_acc, self.lse_acc, self.o_step,

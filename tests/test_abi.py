@@ -127,6 +127,12 @@ def test_calls_reject_before_device_work():
     with pytest.raises(B.RaError) as e:
         B.ring_attn_step_bwd(good_desc(), 16, 16, 16, 0, 16, 16, 16, 16, 16, stream=0)
     assert e.value.status == B.RA_EINVAL
+    for args, code in [((d, 16, 16, 16, 16, 16), B.RA_EUNSUPPORTED),
+                       ((good_desc(), 16, 16, 16, 0, 16), B.RA_EINVAL),      # null o_acc
+                       ((good_desc(), 16, 16, 16, 16, 8), B.RA_EALIGN)]:     # misaligned lse_acc
+        with pytest.raises(B.RaError) as e:
+            B.ring_attn_step_fwd_merge(*args, stream=0)
+        assert e.value.status == code
     for call, code in [
         (lambda: B.lse_merge(-1, 4, 128, 16, 16, 16, 16, stream=0), B.RA_EINVAL),
         (lambda: B.lse_merge(8, 4, 80, 16, 16, 16, 16, stream=0), B.RA_EUNSUPPORTED),
@@ -149,6 +155,7 @@ def test_zero_size_calls_are_noops():
     B.ra_fill_f32(0, 0, 1.0, stream=0)
     B.head_permute(0, 0, 0, 8, 128, 4, 2, stream=0)
     B.ring_attn_step_fwd(good_desc(q_segments=((0, 448), 0)), 0, 0, 0, 0, 0, stream=0)
+    B.ring_attn_step_fwd_merge(good_desc(k_segments=((0, 448), 0)), 0, 0, 0, 0, 0, stream=0)
     B.ring_attn_step_bwd(good_desc(k_segments=((0, 448), 0)), 0, 0, 0, 0, 0, 0, 0, 0, 0, stream=0)
 
 

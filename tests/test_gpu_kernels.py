@@ -182,6 +182,44 @@ def test_step_forward_empty_chunk():
 
 
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_step_forward_merge(case):
+    """The fused step + merge, folded over every chunk of the ring, against the
+    oracle's steps merged in fp64, and against the separate GPU calls."""
+    dtype, d, hq, hkv, b, P, r, causal = case
+    S = 2 * P * b
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=79)
+    L = 2 * b
+    q = to_device(x["q"], dtype)
+    kc = to_device(x["k_ch"], dtype)
+    vc = to_device(x["v_ch"], dtype)
+    o_f = torch.zeros((L, hq, d), device="cuda")
+    l_f = torch.full((hq, L), float("-inf"), device="cuda")
+    o_u = torch.zeros((L, hq, d), device="cuda")
+    l_u = torch.full((hq, L), float("-inf"), device="cuda")
+    o_s = torch.empty((L, hq, d), device="cuda")
+    l_s = torch.empty((hq, L), device="cuda")
+    want_o = np.zeros((L, hq, d))
+    want_l = np.full((hq, L), -np.inf)
+    for j in oracle.double_ring_order(P, 1, r):
+        desc = _desc(dtype, d, hq, hkv, S, P, r, int(j), causal)
+        B().ring_attn_step_fwd_merge(desc, q, kc[j], vc[j], o_f, l_f)
+        B().ring_attn_step_fwd(desc, q, kc[j], vc[j], o_s, l_s)
+        B().lse_merge(L, hq, d, o_u, l_u, o_s, l_s)
+        so, sl = _oracle_step_fwd(x, S, P, r, int(j), d, dtype, causal)
+        want_o, want_l = oracle.lse_merge(want_o, want_l, so, sl)
+    torch.cuda.synchronize()
+    got_o, got_l = o_f.cpu().numpy(), l_f.cpu().numpy()
+    assert not np.isnan(got_o).any() and not np.isnan(got_l).any()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(want_l))
+    assert_close("merged O", got_o, want_o, dtype)
+    assert_close("merged LSE", got_l, want_l, dtype, is_lse=True)
+    # the fused epilogue applies the separate merge's formula to the same values
+    fin = np.isfinite(want_l)
+    assert max_abs(got_o, o_u.cpu().numpy()) < 1e-5
+    assert max_abs(got_l[fin], l_u.cpu().numpy()[fin]) < 1e-5
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_step_backward(case):
     dtype, d, hq, hkv, b, P, r, causal = case
     S = 2 * P * b

@@ -27,9 +27,9 @@ def _gpu():
     yield
 
 
-def run_share(S, inner, outer, r, hq, hkv, d, dtype, x):
+def run_share(S, inner, outer, r, hq, hkv, d, dtype, x, merge="fused"):
     from ring_attention_attn_amd.ring import ShareRing
-    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype)
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype, merge=merge)
     q, do = to_device(x["q"], dtype), to_device(x["do"], dtype)
     K, V = to_device(x["k_ch"], dtype), to_device(x["v_ch"], dtype)
     o, lse = ring.forward(q, K, V)
@@ -74,6 +74,20 @@ def test_share_matches_oracle(case):
         for half in (slice(0, b), slice(b, 2 * b)):
             assert rel_l2(got["O"][half], want["O"][half]) < 1e-2
             assert rel_l2(got["dQ"][half], want["dQ"][half]) < 1e-2
+
+
+@pytest.mark.parametrize("case", [SHARE_CASES[1], SHARE_CASES[6]], ids=lambda c: c[0])
+def test_share_separate_merge_matches_fused(case):
+    """The forward with separate lse_merge launches gives the fused result (the
+    same merge formula on the same values, up to fp32 rounding)."""
+    name, S, inner, outer, r, hq, hkv, d, dtype = case
+    x = share_inputs(S, inner * outer, r, hq, hkv, d, dtype, seed=2000 + S + r)
+    _, fused = run_share(S, inner, outer, r, hq, hkv, d, dtype, x, "fused")
+    _, sep = run_share(S, inner, outer, r, hq, hkv, d, dtype, x, "separate")
+    fin = np.isfinite(sep["LSE"])
+    assert np.array_equal(np.isneginf(fused["LSE"]), np.isneginf(sep["LSE"]))
+    assert max_abs(fused["O"], sep["O"]) < 1e-5
+    assert max_abs(fused["LSE"][fin], sep["LSE"][fin]) < 1e-5
 
 
 def test_ring_order_invariance():
