@@ -63,11 +63,12 @@ def recorded_traffic(cfg_name):
     return None
 
 
-def make_inputs(cfg, rank):
+def make_inputs(cfg, rank, layout="zigzag"):
     import torch
     from ring_attention_attn_amd import synth
     P, b = cfg.P, cfg.b
-    mine = synth.paired_blocks(P, rank)
+    blocks_of = synth.paired_blocks if layout == "zigzag" else synth.contiguous_blocks
+    mine = blocks_of(P, rank)
 
     def dev(bits):
         if cfg.dtype == "bf16":
@@ -78,7 +79,7 @@ def make_inputs(cfg, rank):
     do = dev(synth.blocks_tensor(cfg.seed, synth.T_DO, mine, b, cfg.hq, cfg.d, cfg.dtype))
     K, V = [], []
     for j in range(P):
-        blocks = synth.paired_blocks(P, j)
+        blocks = blocks_of(P, j)
         K.append(dev(synth.blocks_tensor(cfg.seed, synth.T_K, blocks, b, cfg.hkv, cfg.d, cfg.dtype)))
         V.append(dev(synth.blocks_tensor(cfg.seed, synth.T_V, blocks, b, cfg.hkv, cfg.d, cfg.dtype)))
     return q, torch.stack(K), torch.stack(V), do
@@ -122,6 +123,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0, help="ring rank whose share is timed")
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("zigzag", "contiguous"), default="zigzag",
+                    help="rows of the share: paired blocks (the method) or one contiguous "
+                         "chunk per rank (to measure the causal imbalance, rank by rank)")
     ap.add_argument("--merge", choices=("fused", "separate"), default="fused",
                     help="fold each forward step into the running result in the forward "
                          "kernel (fused) or with a separate lse_merge launch")
@@ -145,9 +149,9 @@ def main():
     cfg = CONFIGS[args.config]
     log(f"config {cfg.name}: S={cfg.S} P={cfg.P} ({cfg.inner}x{cfg.outer}) hq={cfg.hq} "
         f"hkv={cfg.hkv} d={cfg.d} {cfg.dtype} rank={args.rank}")
-    q, K, V, do = make_inputs(cfg, args.rank)
+    q, K, V, do = make_inputs(cfg, args.rank, args.layout)
     ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d, cfg.dtype,
-                     merge=args.merge)
+                     merge=args.merge, layout=args.layout)
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(7)   # 1 GiB
         dst = torch.empty_like(src)
@@ -205,7 +209,7 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
-    fwd_flops, bwd_flops = cfg.flops()
+    fwd_flops, bwd_flops = cfg.flops(args.layout, args.rank)
     total = fwd_flops + bwd_flops
     ms = wall / args.steps * 1e3
     value = total * args.steps / wall / 1e12
@@ -250,7 +254,8 @@ def main():
         "data": "synthetic (seeded N(0,1), rounded to bf16)",
         "config": {"workload": cfg.name, "global_seq": cfg.S, "ring": f"{cfg.inner}x{cfg.outer}",
                    "local_rows": cfg.rows, "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.d,
-                   "rank": args.rank, "parallelism": "one GPU's share (virtual ring)"},
+                   "rank": args.rank, "layout": args.layout,
+                   "parallelism": "one GPU's share (virtual ring)"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "merge": args.merge,
         "breakdown_ms_per_launch": {"step_fwd": round(fwd_ms, 4), "step_bwd": round(bwd_ms, 4),
@@ -262,7 +267,9 @@ def main():
                      "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(cfg.name)},
     }
-    if not args.no_cpu_baseline:
+    if args.layout != "zigzag":
+        log("cpu baseline is taken on the paired-block share only; skipped")
+    elif not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(cfg, args.rank, args.cpu_rows)
     print(json.dumps(out), flush=True)

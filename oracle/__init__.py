@@ -27,11 +27,11 @@ Every function is pinned by ``tests/test_oracle.py`` (closed forms, invariants,
 a library special case, brute force, finite differences) except where its
 docstring says "parity unpinned".
 """
-from .index_maps import (zigzag_positions, chunk_blocks, double_ring_order,
-                         head_permute, causal_pair_count)
+from .index_maps import (zigzag_positions, contiguous_positions, chunk_blocks,
+                         double_ring_order, head_permute, causal_pair_count)
 from .attention import (share_forward, share_backward, step_forward, step_backward,
                         lse_merge, bf16_bits_to_f64, NEG_INF)
 
-__all__ = ["zigzag_positions", "chunk_blocks", "double_ring_order", "head_permute",
+__all__ = ["zigzag_positions", "contiguous_positions", "chunk_blocks", "double_ring_order", "head_permute",
            "causal_pair_count", "share_forward", "share_backward", "step_forward",
            "step_backward", "lse_merge", "bf16_bits_to_f64", "NEG_INF"]

@@ -34,6 +34,23 @@ def zigzag_positions(S, P, r):
     return np.array(out, dtype=np.int64)
 
 
+def contiguous_positions(S, P, r):
+    """Global token positions of rank ``r``'s rows when the sequence is sliced
+    into P consecutive chunks and rank r holds chunk r (the layout whose causal
+    load imbalance the paired blocks remove): tokens r*S/P .. (r+1)*S/P - 1.
+
+    "Guide to LoongTrain", section "The Communication Overhead and Causal
+    Imbalance of Ring Attention" (P chunks, GPU 0 holding the earliest chunk and
+    GPU P-1 the latest). A KV chunk j uses the same map with r := j.
+    """
+    if not (0 <= r < P):
+        raise ValueError("rank out of range")
+    if S % P != 0:
+        raise ValueError("S must be a multiple of P")
+    L = S // P
+    return np.array([r * L + i for i in range(L)], dtype=np.int64)
+
+
 def causal_pair_count(pos_q, S):
     """Number of visible (query, key) pairs for query rows ``pos_q`` against the
     whole sequence of length S: query at position p sees keys 0..p.

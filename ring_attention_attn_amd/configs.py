@@ -38,13 +38,18 @@ class ShareConfig:
     def scale(self):
         return 1.0 / (self.d ** 0.5)
 
-    def pairs_per_head(self):
-        """Visible (q, k) pairs per query head of any rank: b (S + 1)."""
-        return self.b * (self.S + 1)
+    def pairs_per_head(self, layout="zigzag", rank=0):
+        """Visible (q, k) pairs per query head of a rank's share: b (S + 1) for
+        every rank with paired blocks; with contiguous chunks of L = S/P rows,
+        rank r's rows r*L .. r*L+L-1 see L (r L) + L (L + 1) / 2 pairs."""
+        if layout == "zigzag":
+            return self.b * (self.S + 1)
+        L = self.S // self.P
+        return L * rank * L + L * (L + 1) // 2
 
-    def flops(self):
+    def flops(self, layout="zigzag", rank=0):
         """Algorithmic fwd+bwd flops of the share: 4 d Hq N (fwd) + 10 d Hq N (bwd)."""
-        n = self.pairs_per_head()
+        n = self.pairs_per_head(layout, rank)
         return 4 * self.d * self.hq * n, 10 * self.d * self.hq * n
 
 

@@ -26,19 +26,31 @@ class ShareRing:
 
     Inputs (caller-owned, contiguous): q [L][hq][d], K/V [P][L][hkv][d] (chunk j
     = rows of blocks j and 2P-1-j), dout [L][hq][d]; L = 2b rows, b = S/(2P).
+    layout="contiguous" instead gives rank r (and chunk j) the L consecutive
+    tokens r*L .. r*L+L-1, the layout whose causal imbalance the paired blocks
+    remove; the kernels are the same (one segment instead of two).
     """
 
     def __init__(self, S, inner, outer, rank, hq, hkv, d, dtype="bf16", scale=None,
-                 device="cuda", causal=1, merge="fused"):
+                 device="cuda", causal=1, merge="fused", layout="zigzag"):
         if merge not in ("fused", "separate"):
             raise ValueError(f"merge must be 'fused' or 'separate', not {merge!r}")
-        self.merge = merge
+        if layout not in ("zigzag", "contiguous"):
+            raise ValueError(f"layout must be 'zigzag' or 'contiguous', not {layout!r}")
+        self.merge, self.layout = merge, layout
         self.S, self.inner, self.outer, self.rank = S, inner, outer, rank
         self.P = inner * outer
         self.hq, self.hkv, self.d, self.dtype = hq, hkv, d, dtype
         self.scale = scale if scale is not None else d ** -0.5
-        q_seg, b = B.ra_zigzag_segments(S, self.P, rank)
-        self.L = 2 * b
+        def segments(r):
+            # zigzag: two paired blocks of b rows; contiguous: one chunk of 2b rows
+            if layout == "zigzag":
+                return B.ra_zigzag_segments(S, self.P, r)
+            L = S // self.P
+            return (r * L,), L
+
+        q_seg, b = segments(rank)
+        self.L = 2 * b if layout == "zigzag" else b
         self.order = [int(j) for j in B.ra_double_ring_order(inner, outer, rank)]
         f32 = dict(dtype=torch.float32, device=device)
         L = self.L
@@ -53,7 +65,7 @@ class ShareRing:
         self.o_lowp = torch.empty((L, hq, d), dtype=torch.bfloat16, device=device)
         self.descs = []
         for j in self.order:
-            k_seg, kb = B.ra_zigzag_segments(S, self.P, j)
+            k_seg, kb = segments(j)
             desc = B.make_desc(dtype=_RA_DTYPE[dtype], head_dim=d, hq=hq, hkv=hkv,
                                q_segments=(q_seg, b), k_segments=(k_seg, kb), scale=self.scale,
                                causal=causal, q_strides=(hq * d, d), k_strides=(hkv * d, d),

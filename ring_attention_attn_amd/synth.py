@@ -50,6 +50,13 @@ def blocks_tensor(seed, tensor_id, blocks, b, H, d, dtype):
     raise ValueError("dtype must be 'bf16' or 'f32'")
 
 
+def contiguous_blocks(P, r):
+    """Natural block ids (2P blocks of S/2P rows) whose rows rank r holds when
+    the sequence is cut into P consecutive chunks: blocks 2r and 2r+1. Pure
+    bookkeeping of which draws to take, as for paired_blocks."""
+    return [2 * r, 2 * r + 1]
+
+
 def paired_blocks(P, r):
     """Natural block ids (2P blocks in all) whose rows a ring chunk r holds, in
     row order: the front block r, then the back block 2P-1-r. Pure bookkeeping

@@ -4,7 +4,7 @@ import numpy as np
 from ring_attention_attn_amd import synth
 
 
-def share_inputs(S, P, r, hq, hkv, d, dtype, seed):
+def share_inputs(S, P, r, hq, hkv, d, dtype, seed, layout="zigzag"):
     """Seeded inputs of rank r's share.
 
     Returns a dict of host arrays in the input dtype (uint16 bf16 bits or
@@ -12,15 +12,18 @@ def share_inputs(S, P, r, hq, hkv, d, dtype, seed):
     [P][L][hkv][d] (chunk j = blocks j, 2P-1-j), and the natural-order K/V
     [S][hkv][d]; plus fp64 widenings (exact) for the oracle."""
     b = S // (2 * P)
-    mine = synth.paired_blocks(P, r)
+    blocks_of = synth.paired_blocks if layout == "zigzag" else synth.contiguous_blocks
+    mine = blocks_of(P, r)
     q = synth.blocks_tensor(seed, synth.T_Q, mine, b, hq, d, dtype)
     do = synth.blocks_tensor(seed, synth.T_DO, mine, b, hq, d, dtype)
     k_nat = synth.blocks_tensor(seed, synth.T_K, range(2 * P), b, hkv, d, dtype)
     v_nat = synth.blocks_tensor(seed, synth.T_V, range(2 * P), b, hkv, d, dtype)
-    k_ch = np.stack([np.concatenate([k_nat[j * b:(j + 1) * b],
-                                     k_nat[(2 * P - 1 - j) * b:(2 * P - j) * b]]) for j in range(P)])
-    v_ch = np.stack([np.concatenate([v_nat[j * b:(j + 1) * b],
-                                     v_nat[(2 * P - 1 - j) * b:(2 * P - j) * b]]) for j in range(P)])
+
+    def chunk(nat, j):
+        return np.concatenate([nat[blk * b:(blk + 1) * b] for blk in blocks_of(P, j)])
+
+    k_ch = np.stack([chunk(k_nat, j) for j in range(P)])
+    v_ch = np.stack([chunk(v_nat, j) for j in range(P)])
     return dict(q=q, do=do, k_nat=k_nat, v_nat=v_nat, k_ch=k_ch, v_ch=v_ch, b=b)
 
 

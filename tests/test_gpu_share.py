@@ -27,9 +27,9 @@ def _gpu():
     yield
 
 
-def run_share(S, inner, outer, r, hq, hkv, d, dtype, x, merge="fused"):
+def run_share(S, inner, outer, r, hq, hkv, d, dtype, x, merge="fused", layout="zigzag"):
     from ring_attention_attn_amd.ring import ShareRing
-    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype, merge=merge)
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype, merge=merge, layout=layout)
     q, do = to_device(x["q"], dtype), to_device(x["do"], dtype)
     K, V = to_device(x["k_ch"], dtype), to_device(x["v_ch"], dtype)
     o, lse = ring.forward(q, K, V)
@@ -88,6 +88,28 @@ def test_share_separate_merge_matches_fused(case):
     assert np.array_equal(np.isneginf(fused["LSE"]), np.isneginf(sep["LSE"]))
     assert max_abs(fused["O"], sep["O"]) < 1e-5
     assert max_abs(fused["LSE"][fin], sep["LSE"][fin]) < 1e-5
+
+
+@pytest.mark.parametrize("r", [0, 1, 3])
+def test_contiguous_layout_share(r):
+    """One contiguous chunk per rank (the layout whose causal imbalance the
+    paired blocks remove): same kernels, one segment per map."""
+    S, inner, outer, hq, hkv, d, dtype = 4096, 4, 1, 8, 2, 128, "bf16"
+    P = inner * outer
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=3000 + r, layout="contiguous")
+    _, got = run_share(S, inner, outer, r, hq, hkv, d, dtype, x, layout="contiguous")
+    pos = oracle.contiguous_positions(S, P, r)
+    want = oracle.share_backward(widen(x["q"], dtype), widen(x["k_nat"], dtype),
+                                 widen(x["v_nat"], dtype), widen(x["do"], dtype), pos, 1 / math.sqrt(d))
+    assert_close("O", got["O"], want["O"], dtype)
+    assert_close("LSE", got["LSE"], want["LSE"], dtype, is_lse=True)
+    assert_close("dQ", got["dQ"], want["dQ"], dtype)
+    for j in range(P):
+        kp = oracle.contiguous_positions(S, P, j)
+        assert_close(f"dK[{j}]", got["dK"][j], want["dK"][kp], dtype)
+        assert_close(f"dV[{j}]", got["dV"][j], want["dV"][kp], dtype)
+    assert rel_l2(got["O"], want["O"]) < 1e-2
+    assert rel_l2(got["dQ"], want["dQ"]) < 1e-2
 
 
 def test_ring_order_invariance():

@@ -374,3 +374,26 @@ def test_bf16_widening_exact():
     vals = oracle.bf16_bits_to_f64(bits)
     assert vals[0] == 1.0 and vals[1] == -1.0 and vals[2] == 0.0 and np.isposinf(vals[3])
     assert vals[4] == 3.140625
+
+
+@pytest.mark.parametrize("S,P", [(64, 4), (96, 3), (4096, 8)])
+def test_contiguous_layout_pairs_and_imbalance(S, P):
+    """Contiguous chunks partition the sequence; rank r's pair count is
+    L (r L) + L (L + 1) / 2 (brute force), so the latest rank does (2P - 1)
+    times the earliest one's work up to O(1/L) -- the imbalance the paired
+    blocks remove (every paired-block rank has b (S + 1))."""
+    from ring_attention_attn_amd.configs import ShareConfig
+    L = S // P
+    allpos = np.concatenate([oracle.contiguous_positions(S, P, r) for r in range(P)])
+    assert np.array_equal(np.sort(allpos), np.arange(S))
+    cfg = ShareConfig("t", S=S, inner=P, outer=1, hq=1, hkv=1, d=64, dtype="f32", seed=0)
+    counts = []
+    for r in range(P):
+        pos = oracle.contiguous_positions(S, P, r)
+        brute = sum(1 for p in pos for k in range(S) if k <= p)
+        assert oracle.causal_pair_count(pos, S) == brute == cfg.pairs_per_head("contiguous", r)
+        counts.append(brute)
+        assert cfg.pairs_per_head("zigzag", r) == oracle.causal_pair_count(
+            oracle.zigzag_positions(S, P, r), S)
+    assert counts[-1] * (L + 1) == counts[0] * (2 * (P - 1) * L + L + 1)
+    assert sum(counts) == S * (S + 1) // 2
