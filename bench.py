@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--layout", choices=("zigzag", "contiguous"), default="zigzag",
                     help="rows of the share: paired blocks (the method) or one contiguous "
                          "chunk per rank (to measure the causal imbalance, rank by rank)")
+    ap.add_argument("--kv-rings", choices=("one", "ab"), default="one",
+                    help="one launch per ring step, or two (one per block of the KV chunk: "
+                         "the block A and block B rings)")
     ap.add_argument("--merge", choices=("fused", "separate"), default="fused",
                     help="fold each forward step into the running result in the forward "
                          "kernel (fused) or with a separate lse_merge launch")
@@ -151,7 +154,7 @@ def main():
         f"hkv={cfg.hkv} d={cfg.d} {cfg.dtype} rank={args.rank}")
     q, K, V, do = make_inputs(cfg, args.rank, args.layout)
     ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d, cfg.dtype,
-                     merge=args.merge, layout=args.layout)
+                     merge=args.merge, layout=args.layout, kv_rings=args.kv_rings)
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(7)   # 1 GiB
         dst = torch.empty_like(src)
@@ -172,15 +175,16 @@ def main():
     from ring_attention_attn_amd import binding as B
 
     def timed_step():
-        for t, (j, desc) in enumerate(ring.descs):
+        for t, (j, off, desc) in enumerate(ring.launches):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             fused = t > 0 and args.merge == "fused"
             o, l = (ring.o_acc, ring.lse_acc) if t == 0 or fused else (ring.o_step, ring.lse_step)
+            k, v = ring._kv(K, j, off), ring._kv(V, j, off)
             e0.record(stream)
             if fused:
-                B.ring_attn_step_fwd_merge(desc, q, K[j], V[j], o, l)
+                B.ring_attn_step_fwd_merge(desc, q, k, v, o, l)
             else:
-                B.ring_attn_step_fwd(desc, q, K[j], V[j], o, l)
+                B.ring_attn_step_fwd(desc, q, k, v, o, l)
             e1.record(stream)
             ev["fwd"].append((e0, e1))
             if t > 0 and not fused:
@@ -193,11 +197,12 @@ def main():
         B.ra_bwd_delta(ring.L, ring.hq, ring.d, B.RA_BF16 if cfg.dtype == "bf16" else B.RA_F32,
                        ring.o_acc, do, ring.delta, ring.o_lowp if cfg.dtype == "bf16" else None)
         B.ra_fill_f32(ring.dq, ring.dq.numel(), 0.0)
-        for j, desc in ring.descs:
+        for j, off, desc in ring.launches:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            B.ring_attn_step_bwd(desc, q, K[j], V[j], do, ring.lse_acc, ring.delta, ring.dq,
-                                 ring.dk[j], ring.dv[j])
+            B.ring_attn_step_bwd(desc, q, ring._kv(K, j, off), ring._kv(V, j, off), do,
+                                 ring.lse_acc, ring.delta, ring.dq, ring._kv(ring.dk, j, off),
+                                 ring._kv(ring.dv, j, off))
             e1.record(stream)
             ev["bwd"].append((e0, e1))
 
@@ -234,8 +239,9 @@ def main():
     fwd_ms, bwd_ms, merge_ms = avg_ms(ev["fwd"]), avg_ms(ev["bwd"]), avg_ms(ev["merge"])
     # algorithmic flops per launch: each ring step carries 1/P of the share's pairs
     # (2b^2 per head per step, +b on the diagonal step); averaged over the P launches
-    bwd_launch_flops = bwd_flops / cfg.P
-    fwd_launch_flops = fwd_flops / cfg.P
+    n_launch = len(ring.launches)   # P, or 2P with the block A / block B rings
+    bwd_launch_flops = bwd_flops / n_launch
+    fwd_launch_flops = fwd_flops / n_launch
     bwd_tflops = bwd_launch_flops / (bwd_ms * 1e-3) / 1e12
     fwd_tflops = fwd_launch_flops / (fwd_ms * 1e-3) / 1e12
     merge_bytes = cfg.rows * cfg.hq * (cfg.d * 4 * 3 + 4 * 3)
@@ -254,7 +260,7 @@ def main():
         "data": "synthetic (seeded N(0,1), rounded to bf16)",
         "config": {"workload": cfg.name, "global_seq": cfg.S, "ring": f"{cfg.inner}x{cfg.outer}",
                    "local_rows": cfg.rows, "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.d,
-                   "rank": args.rank, "layout": args.layout,
+                   "rank": args.rank, "layout": args.layout, "kv_rings": args.kv_rings,
                    "parallelism": "one GPU's share (virtual ring)"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "merge": args.merge,

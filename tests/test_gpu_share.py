@@ -112,6 +112,39 @@ def test_contiguous_layout_share(r):
     assert rel_l2(got["dQ"], want["dQ"]) < 1e-2
 
 
+@pytest.mark.parametrize("case", [SHARE_CASES[4], SHARE_CASES[7]], ids=lambda c: c[0])
+def test_ab_rings_share(case):
+    """Each step as two launches, one per block of the KV chunk (the block A and
+    block B rings), against the oracle and the one-launch steps."""
+    name, S, inner, outer, r, hq, hkv, d, dtype = case
+    P = inner * outer
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=4000 + S + r)
+    from ring_attention_attn_amd.ring import ShareRing
+    q, do = to_device(x["q"], dtype), to_device(x["do"], dtype)
+    K, V = to_device(x["k_ch"], dtype), to_device(x["v_ch"], dtype)
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype, kv_rings="ab")
+    assert len(ring.launches) == 2 * P
+    o, lse = ring.forward(q, K, V)
+    dq, dk, dv = ring.backward(q, K, V, do)
+    torch.cuda.synchronize()
+    pos = oracle.zigzag_positions(S, P, r)
+    want = oracle.share_backward(widen(x["q"], dtype), widen(x["k_nat"], dtype),
+                                 widen(x["v_nat"], dtype), widen(x["do"], dtype), pos, 1 / math.sqrt(d))
+    assert_close("O", o.cpu().numpy(), want["O"], dtype)
+    assert_close("LSE", lse.cpu().numpy(), want["LSE"], dtype, is_lse=True)
+    assert_close("dQ", dq.cpu().numpy(), want["dQ"], dtype)
+    for j in range(P):
+        kp = oracle.zigzag_positions(S, P, j)
+        assert_close(f"dK[{j}]", dk[j].cpu().numpy(), want["dK"][kp], dtype)
+        assert_close(f"dV[{j}]", dv[j].cpu().numpy(), want["dV"][kp], dtype)
+    # against the one-launch steps: a half-chunk step rounds P to bf16 under its
+    # own exponent shift, so O (and, through D, the gradients) differ at the
+    # level of that rounding, not of fp32
+    _, one = run_share(S, inner, outer, r, hq, hkv, d, dtype, x)
+    assert max_abs(o.cpu().numpy(), one["O"]) < 2e-3
+    assert max_abs(dk.cpu().numpy(), one["dK"]) < 2e-3
+
+
 def test_ring_order_invariance():
     """The merged result does not depend on the order the chunks are visited in
     (up to fp32 rounding of the merge)."""
@@ -123,7 +156,7 @@ def test_ring_order_invariance():
     K, V = to_device(x["k_ch"], "bf16"), to_device(x["v_ch"], "bf16")
     ring = ShareRing(S, inner, outer, r, hq, hkv, d, "bf16")
     o1 = ring.forward(q, K, V)[0].clone()
-    ring.descs = ring.descs[::-1]
+    ring.launches = ring.launches[::-1]
     o2 = ring.forward(q, K, V)[0].clone()
     torch.cuda.synchronize()
     assert max_abs(o1.cpu().numpy(), o2.cpu().numpy()) < 1e-5
