@@ -475,18 +475,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
 #pragma unroll
   for (int db = 0; db < ND; ++db) acc[db] = f32x16{};
 
-  // iterations: (query head of the group hh, query tile t) pairs, hh-major;
+  // iterations: (query tile t, query head of the group hh) pairs, tiles in
+  // descending order with the heads innermost, so the workgroups of one KV
+  // head read the same Q / dO tiles at about the same time until each reaches
+  // its first visible tile (the visible tiles are suffixes, different for each
+  // key block on the diagonal step; a shared order keeps them in L2);
   // hh == group marks the end
   const QueryTiles<QT> qt_wg(p.qm, p.causal, gk_lo, gk_hi);
   const QueryTiles<QT> qt_w(p.qm, p.causal, wk_lo, wk_hi);
-  const int t_first = qt_wg.next(0);
-  // the visible tile after (hh, t), or (group, 0)
+  const int t_last = qt_wg.prev(qt_wg.n - 1);
+  // the visible (tile, head) after (t, hh), or (-1, group)
   auto advance = [&](int& hh, int& t) {
-    t = qt_wg.next(t + 1);
-    if (t >= qt_wg.n) {
-      ++hh;
-      t = t_first;
-    }
+    if (++hh < p.group) return;
+    t = qt_wg.prev(t - 1);
+    hh = t >= 0 ? 0 : p.group;
   };
 
   DmaSwz<QT, D, NW, 2> qst, gst;
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   // ago. The two roles run
   // separate loops with the same barrier sequence, so each role's registers
   // are allocated on their own.
-  int ch = t_first < qt_wg.n ? 0 : p.group, ct = t_first;  // tile i
+  int ch = t_last >= 0 ? 0 : p.group, ct = t_last;  // tile i
   int nh = ch, nt = ct;                                    // tile i + 1
   if (ch < p.group) advance(nh, nt);
   bool have_prev = false;

@@ -451,6 +451,13 @@ struct QueryTiles {
     if (t < a1) return t;
     return t > b0 ? (t < n ? t : n) : (b0 < n ? b0 : n);
   }
+  // last visible tile at or before t (-1 if none)
+  __host__ __device__ __forceinline__ int prev(int t) const {
+    if (t >= n) t = n - 1;
+    if (t >= b0) return t;  // in the second run's suffix [b0, n)
+    if (t >= a1) t = a1 - 1;  // between the runs: the first run's last tile
+    return t >= a0 ? t : -1;
+  }
   __device__ __forceinline__ bool mask_free(int t) const {
     const int r0 = t * TQ, r1 = r0 + TQ;
     if (r1 > len) return false;
