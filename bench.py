@@ -29,7 +29,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
-PEAK_HBM_GBS = 8000.0
 
 
 def log(msg):

@@ -103,6 +103,55 @@ def _ptr(x):
     return x.data_ptr()
 
 
+def _extent(rows, heads, ss, hs, d, eb):
+    """Bytes from the base pointer that a [rows][heads][d] tensor with element
+    strides (ss, hs) spans."""
+    if rows <= 0 or heads <= 0:
+        return 0
+    return ((rows - 1) * ss + (heads - 1) * hs + d) * eb
+
+
+def _arg(x, name, nbytes, dtype=None, elem_bytes=None):
+    """Check a tensor argument before its pointer reaches a kernel: on the GPU,
+    of the expected dtype ("bf16" / "f32") or element size, holding at least
+    ``nbytes`` from its data pointer. Raw integer pointers pass unchecked."""
+    if x is None or isinstance(x, int) or nbytes <= 0:
+        return
+    import torch
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {x.device})")
+    if dtype is not None:
+        want = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+        if x.dtype != want:
+            raise ValueError(f"{name} must be {want} (got {x.dtype})")
+    if elem_bytes is not None and x.element_size() != elem_bytes:
+        raise ValueError(f"{name} must have {elem_bytes}-byte elements (got {x.dtype})")
+    have = x.untyped_storage().nbytes() - x.storage_offset() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: the call addresses {nbytes} bytes from its data pointer, "
+                         f"the tensor holds {have}")
+
+
+def _step_args(desc, for_bwd, q, k, v, o, lse, dout=None, delta=None, dk=None, dv=None):
+    """Tensor checks of the step calls, done only for a descriptor the library
+    accepts (an invalid one is left to the library's own status)."""
+    if lib().ra_validate_step(ctypes.byref(desc), int(for_bwd)) != RA_OK:
+        return
+    dt = "bf16" if desc.dtype == RA_BF16 else "f32"
+    eb = 2 if dt == "bf16" else 4
+    D, lq, lk = desc.head_dim, desc.q_nseg * desc.q_seg_len, desc.k_nseg * desc.k_seg_len
+    _arg(q, "q", _extent(lq, desc.hq, desc.q_ss, desc.q_hs, D, eb), dt)
+    _arg(k, "k", _extent(lk, desc.hkv, desc.k_ss, desc.k_hs, D, eb), dt)
+    _arg(v, "v", _extent(lk, desc.hkv, desc.v_ss, desc.v_hs, D, eb), dt)
+    _arg(o, "o", _extent(lq, desc.hq, desc.o_ss, desc.o_hs, D, 4), "f32")
+    _arg(lse, "lse", desc.hq * lq * 4, "f32")
+    if for_bwd:
+        _arg(dout, "dout", _extent(lq, desc.hq, desc.do_ss, desc.do_hs, D, eb), dt)
+        _arg(delta, "delta", desc.hq * lq * 4, "f32")
+        _arg(dk, "dk_acc", _extent(lk, desc.hkv, desc.dk_ss, desc.dk_hs, D, 4), "f32")
+        _arg(dv, "dv_acc", _extent(lk, desc.hkv, desc.dk_ss, desc.dk_hs, D, 4), "f32")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -115,38 +164,55 @@ def _stream(stream):
 # ---------------------------------------------------------------- device calls
 
 def ring_attn_step_fwd(desc, q, k, v, o_step, lse_step, stream=None):
+    _step_args(desc, 0, q, k, v, o_step, lse_step)
     _check(lib().ring_attn_step_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o_step),
                                     _ptr(lse_step), _stream(stream)), "ring_attn_step_fwd")
 
 
 def ring_attn_step_fwd_merge(desc, q, k, v, o_acc, lse_acc, stream=None):
+    _step_args(desc, 0, q, k, v, o_acc, lse_acc)
     _check(lib().ring_attn_step_fwd_merge(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(o_acc), _ptr(lse_acc), _stream(stream)),
            "ring_attn_step_fwd_merge")
 
 
 def ring_attn_step_bwd(desc, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, stream=None):
+    _step_args(desc, 1, q, k, v, dq_acc, lse, dout, delta, dk_acc, dv_acc)
     _check(lib().ring_attn_step_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                     _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
                                     _ptr(dv_acc), _stream(stream)), "ring_attn_step_bwd")
 
 
 def lse_merge(rows, hq, head_dim, o_acc, lse_acc, o_step, lse_step, stream=None):
+    if rows > 0 and hq > 0:
+        for x, name, n in ((o_acc, "o_acc", rows * hq * head_dim), (o_step, "o_step", rows * hq * head_dim),
+                           (lse_acc, "lse_acc", hq * rows), (lse_step, "lse_step", hq * rows)):
+            _arg(x, name, 4 * n, "f32")
     _check(lib().lse_merge(rows, hq, head_dim, _ptr(o_acc), _ptr(lse_acc), _ptr(o_step),
                            _ptr(lse_step), _stream(stream)), "lse_merge")
 
 
 def ra_bwd_delta(rows, hq, head_dim, dtype, o, dout, delta, o_out=None, stream=None):
+    if rows > 0 and hq > 0 and dtype in (RA_BF16, RA_F32):
+        n = rows * hq * head_dim
+        _arg(o, "o", 4 * n, "f32")
+        _arg(dout, "dout", (2 if dtype == RA_BF16 else 4) * n, "bf16" if dtype == RA_BF16 else "f32")
+        _arg(delta, "delta", 4 * hq * rows, "f32")
+        _arg(o_out, "o_out", 2 * n, "bf16")
     _check(lib().ra_bwd_delta(rows, hq, head_dim, dtype, _ptr(o), _ptr(dout), _ptr(delta),
                               _ptr(o_out), _stream(stream)), "ra_bwd_delta")
 
 
 def head_permute(src, dst, s, h, d, p, elem_bytes, inverse=0, stream=None):
+    if s > 0 and h > 0 and d > 0 and elem_bytes in (2, 4):  # a bit copy: any dtype of that size
+        _arg(src, "src", s * h * d * elem_bytes, elem_bytes=elem_bytes)
+        _arg(dst, "dst", s * h * d * elem_bytes, elem_bytes=elem_bytes)
     _check(lib().head_permute(_ptr(src), _ptr(dst), s, h, d, p, elem_bytes, int(inverse),
                               _stream(stream)), "head_permute")
 
 
 def ra_fill_f32(dst, n, value, stream=None):
+    _arg(dst, "dst", 4 * n, "f32")
     _check(lib().ra_fill_f32(_ptr(dst), n, float(value), _stream(stream)), "ra_fill_f32")
 
 

@@ -17,8 +17,9 @@ ra_status check_strides(int64_t ss, int64_t hs, int64_t rows, int32_t heads, int
   if (ss < 0 || hs < 0) return RA_EINVAL;
   if (heads > 1 && hs < d) return RA_EINVAL;
   if (rows > 1 && ss < d) return RA_EINVAL;
-  // one of the two nestings: [rows][heads][d] or [heads][rows][d] (padding allowed)
-  if (rows > 1 && heads > 1 && ss < hs * (int64_t)heads && hs < ss * rows) return RA_EINVAL;
+  // one of the two nestings: [rows][heads][d] (ss >= hs * heads) or [heads][rows][d]
+  // (hs >= ss * rows), padding allowed; written as divisions so no product overflows
+  if (rows > 1 && heads > 1 && ss / heads < hs && hs / rows < ss) return RA_EINVAL;
   int64_t per16 = 16 / eb;
   if ((ss % per16) != 0 || (hs % per16) != 0) return RA_EALIGN;
   return RA_OK;

@@ -19,18 +19,6 @@
 #include "ra_internal.h"
 #include "ra_tile.h"
 
-// minimum resident workgroups per CU of the dQ kernel
-#ifndef RA_BWD_DQ_MINB
-#define RA_BWD_DQ_MINB 2
-#endif
-// 1: transposed operand tiles staged in LDS; 0: read with ds_read_b64_tr_b16
-#ifndef RA_BWD_KTT
-#define RA_BWD_KTT 0
-#endif
-#ifndef RA_BWD_QTT
-#define RA_BWD_QTT 0
-#endif
-
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;

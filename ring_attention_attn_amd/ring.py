@@ -17,7 +17,6 @@ import torch
 
 from . import binding as B
 
-_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 _RA_DTYPE = {"bf16": B.RA_BF16, "f32": B.RA_F32}
 
 
@@ -85,11 +84,10 @@ class ShareRing:
                 self.launches.append((j, 0, desc(k_seg, kb, 0)))
             else:
                 # two rings, one carrying block A and one block B of each chunk
-                # (each a one-segment key map; the second half accumulates dK/dV
-                # into its own rows, which no other launch touches)
+                # (each a one-segment key map; each launch writes dK/dV of its
+                # own block's rows, which no other launch touches)
                 self.launches.append((j, 0, desc((k_seg[0],), kb, 0)))
                 self.launches.append((j, kb, desc((k_seg[1],), kb, 0)))
-
 
     def _kv(self, X, j, off):
         return X[j] if off == 0 else X[j][off:]

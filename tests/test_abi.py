@@ -79,6 +79,9 @@ def test_validation_accepts_good_descriptor():
     assert B.ra_validate_step(good_desc(), 1) == B.RA_OK
     # head-major layout is a valid nesting too
     assert B.ra_validate_step(good_desc(q_strides=(128, 128 * 128), o_strides=(128, 128 * 128)), 0) == B.RA_OK
+    # very large (padded) strides in either nesting
+    assert B.ra_validate_step(good_desc(q_strides=(2**62, 128)), 0) == B.RA_OK
+    assert B.ra_validate_step(good_desc(q_strides=(128, 2**62)), 0) == B.RA_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -96,6 +99,7 @@ def test_validation_accepts_good_descriptor():
     (dict(q_strides=(1028, 128)), B.RA_EALIGN),     # rows not 16-byte aligned
     (dict(o_strides=(1026, 128)), B.RA_EALIGN),
     (dict(q_strides=(512, 128)), B.RA_EINVAL),      # rows overlap heads
+    (dict(q_strides=(2**60, 2**58)), B.RA_EINVAL),  # overlap; rows * ss would overflow int64
 ])
 def test_validation_rejects(kw, code):
     if code is None:
@@ -170,3 +174,23 @@ def test_binding_rejects_non_contiguous_tensors():
     with pytest.raises(ValueError):
         B._ptr(t)
     assert B._ptr(torch.zeros(4)) != 0
+
+
+def test_binding_rejects_host_tensors():
+    """A host tensor never reaches a kernel: the binding refuses it before the call."""
+    import torch
+    d = good_desc()
+    q = torch.zeros((128, 8, 128), dtype=torch.bfloat16)
+    k = torch.zeros((128, 2, 128), dtype=torch.bfloat16)
+    o = torch.zeros((128, 8, 128))
+    lse = torch.zeros((8, 128))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.ring_attn_step_fwd(d, q, k, k, o, lse, stream=0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.ring_attn_step_fwd_merge(d, q, k, k, o, lse, stream=0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.ra_fill_f32(o, o.numel(), 0.0, stream=0)
+    # an invalid descriptor is reported by the library's own status, as before
+    with pytest.raises(B.RaError) as e:
+        B.ring_attn_step_fwd(good_desc(head_dim=96), q, k, k, o, lse, stream=0)
+    assert e.value.status == B.RA_EUNSUPPORTED

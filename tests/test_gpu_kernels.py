@@ -181,6 +181,35 @@ def test_step_forward_empty_chunk():
     assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
 
 
+def test_binding_checks_tensor_arguments():
+    """Wrong dtype or too few bytes for what the descriptor addresses: the
+    binding raises before any launch."""
+    d, hq, hkv, S, P, r = 128, 4, 2, 512, 2, 0
+    desc = _desc("bf16", d, hq, hkv, S, P, r, 1, 1)
+    L = S // P
+    q = torch.zeros((L, hq, d), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((L, hkv, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((L, hq, d), device="cuda")
+    lse = torch.zeros((hq, L), device="cuda")
+    with pytest.raises(ValueError, match="must be torch.float32"):
+        B().ring_attn_step_fwd(desc, q, kv, kv, o.to(torch.bfloat16), lse)
+    with pytest.raises(ValueError, match="must be torch.bfloat16"):
+        B().ring_attn_step_fwd(desc, q.float(), kv, kv, o, lse)
+    # (fresh tensors: a view is checked against the memory of its whole storage)
+    with pytest.raises(ValueError, match="the call addresses"):
+        B().ring_attn_step_fwd(desc, q[: L // 2].clone(), kv, kv, o, lse)
+    dk = torch.zeros((L, hkv, d), device="cuda")
+    with pytest.raises(ValueError, match="the call addresses"):
+        B().ring_attn_step_bwd(desc, q, kv, kv, q, lse, lse[:, 1:].clone(), o, dk, dk)
+    with pytest.raises(ValueError, match="the call addresses"):
+        B().ring_attn_step_bwd(desc, q, kv, kv, q, lse, lse, o, dk, dk[1:].clone())
+    with pytest.raises(ValueError, match="the call addresses"):
+        B().ra_fill_f32(lse, lse.numel() + 1, 0.0)
+    # the same call with matching tensors runs
+    B().ring_attn_step_fwd(desc, q, kv, kv, o, lse)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_step_forward_merge(case):
     """The fused step + merge, folded over every chunk of the ring, against the
