@@ -49,6 +49,9 @@ SHARE_CASES = [
     ("gqa4_ring4_r3", 8192, 4, 1, 3, 8, 2, 128, "bf16"),
     ("gqa8_double_ring_4x2_r5", 4096, 4, 2, 5, 8, 1, 128, "bf16"),
     ("mha_ring8_ragged_r6", 8 * 2 * 88, 8, 1, 6, 4, 4, 64, "bf16"),
+    # a ring of one rank: the whole causal sequence in one (diagonal) step
+    ("single_rank_p1", 1024, 1, 1, 0, 8, 2, 128, "bf16"),
+    ("single_rank_p1_ragged_d64", 600, 1, 1, 0, 4, 4, 64, "bf16"),
 ]
 
 
