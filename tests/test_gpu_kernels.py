@@ -123,6 +123,8 @@ STEP_CASES = [
     ("bf16", 128, 8, 1, 256, 2, 0, 1),    # GQA 8
     ("bf16", 128, 4, 2, 130, 2, 1, 1),    # GQA 2, tiles crossing the segment boundary
     ("bf16", 128, 4, 1, 72, 2, 0, 0),     # non-causal
+    ("bf16", 128, 6, 2, 130, 2, 1, 1),    # GQA 3 (one head per row block), ragged
+    ("bf16", 64, 8, 1, 100, 3, 1, 1),     # GQA 8 at d=64, ragged
     ("f32", 64, 1, 1, 64, 4, 3, 1),       # the fp32 workload's shape
     ("f32", 128, 4, 2, 40, 2, 1, 1),
 ]
