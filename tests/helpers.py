@@ -46,7 +46,8 @@ def max_abs(a, b):
     if a.size == 0:
         return 0.0
     both_ninf = np.isneginf(a) & np.isneginf(b)
-    diff = np.where(both_ninf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):  # -inf - -inf: masked by both_ninf
+        diff = np.where(both_ninf, 0.0, np.abs(a - b))
     return float(np.nanmax(np.where(np.isnan(diff), np.inf, diff)))
 
 
