@@ -209,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
 
   const int nsub = p.group / hpw;
   const int total = p.hkv * nsub * n_qt;
-  const int logical = xcd_remap(blockIdx.x, total);
+  const int logical = xcd_remap(blockIdx.x, total, p.hkv * nsub);
   const int gh = logical / n_qt;
   const int qt = n_qt - 1 - (logical % n_qt);
   const int g = gh / nsub, hs = gh % nsub;
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   const int l32 = lane & 31, hi = lane >> 5;
   const int srow = sigma32(l32);
 
-  const int logical = xcd_remap(blockIdx.x, p.hkv * n_kt);
+  const int logical = xcd_remap(blockIdx.x, p.hkv * n_kt, p.hkv);
   const int g = logical / n_kt;
   const int kt = logical % n_kt;  // earlier keys (seen by more queries) first
   const int64_t lq = p.qm.len, lk = p.km.len;

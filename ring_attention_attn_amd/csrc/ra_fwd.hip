@@ -181,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   // share an XCD (and its L2); later (heavier) query tiles start first.
   const int nsub = p.group / hpw;
   const int total = p.hkv * nsub * n_qt;
-  const int logical = xcd_remap(blockIdx.x, total);
+  const int logical = xcd_remap(blockIdx.x, total, p.hkv * nsub);
   const int gh = logical / n_qt;
   const int qt = n_qt - 1 - (logical % n_qt);
   const int g = gh / nsub, hs = gh % nsub;

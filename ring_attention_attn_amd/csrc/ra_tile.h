@@ -489,8 +489,18 @@ struct QMaskBounds {
   }
 };
 
-// Workgroup id -> logical id that keeps consecutive logical ids on one XCD
-// (the dispatcher places workgroup w on XCD w % 8).
-__device__ __forceinline__ int xcd_remap(int w, int total) {
-  return (total % 8 == 0) ? (w % 8) * (total / 8) + (w / 8) : w;
+// Workgroup id -> logical id = group * (total / groups) + tile, where the
+// dispatcher places workgroup w on XCD w % 8 and runs an XCD's workgroups in
+// order of w / 8. With 8 or more groups each XCD gets consecutive logical ids
+// (whole groups, sharing its L2). With fewer (8 % groups == 0), a group spans
+// 8 / groups XCDs and its tiles are dealt to them in turn, so every XCD gets
+// an even share of each tile range: with paired blocks one half of the rows
+// (or keys) of a ring step often has no work, and contiguous ranges would
+// leave whole XCDs idle. A bijection either way.
+__device__ __forceinline__ int xcd_remap(int w, int total, int groups) {
+  if (total % 8 != 0) return w;
+  const int x = w % 8, i = w / 8;
+  if (groups >= 8 || 8 % groups != 0) return x * (total / 8) + i;
+  const int per_group = 8 / groups;  // XCDs per group
+  return (x / per_group) * (total / groups) + i * per_group + x % per_group;
 }
