@@ -137,7 +137,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share on one GPU; --gpus {args.gpus} is not supported "
-              "(no collectives in this build)", file=sys.stderr)
+              "(the library has no collectives)", file=sys.stderr)
         sys.exit(2)
 
     import torch
