@@ -62,17 +62,59 @@ def recorded_traffic(cfg_name):
     return None
 
 
+def recorded_mfma_util(cfg_name):
+    """MFMA-busy share of each step kernel's cycles from the committed counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES over 4 SIMDs x 256 CUs x the kernel's
+    cycles), or None when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"mfma_lds_counters_{cfg_name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if kernel_sources_sha256() not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("mfma_busy_pct:"):
+            return json.loads(line.split(":", 1)[1])
+    return None
+
+
+def _dev(cfg, bits):
+    import torch
+    if cfg.dtype == "bf16":
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(bits).cuda()
+
+
+def make_head_parallel_inputs(cfg, rank):
+    """The 2D-Attention share's inputs with every head: Q and dO of the rank's
+    rows [L][H][d], its own K/V chunk [L][Hkv][d], and the other chunks in head
+    group 0 layout [L][Hkv/hp][d] (as the ring would deliver them)."""
+    from ring_attention_attn_amd import synth
+    P, b, hp = cfg.P, cfg.b, cfg.hp
+    H, Hkv = cfg.hq * hp, cfg.hkv * hp
+    mine = synth.paired_blocks(P, rank)
+    dev = lambda x: _dev(cfg, x)
+    q = dev(synth.blocks_tensor(cfg.seed, synth.T_Q, mine, b, H, cfg.d, cfg.dtype))
+    do = dev(synth.blocks_tensor(cfg.seed, synth.T_DO, mine, b, H, cfg.d, cfg.dtype))
+    k_own = dev(synth.blocks_tensor(cfg.seed, synth.T_K, mine, b, Hkv, cfg.d, cfg.dtype))
+    v_own = dev(synth.blocks_tensor(cfg.seed, synth.T_V, mine, b, Hkv, cfg.d, cfg.dtype))
+    k_rest, v_rest = [], []
+    for j in range(P):
+        blocks = synth.paired_blocks(P, j)
+        k_rest.append(None if j == rank else dev(synth.blocks_tensor(
+            cfg.seed, synth.T_K, blocks, b, cfg.hkv, cfg.d, cfg.dtype)))
+        v_rest.append(None if j == rank else dev(synth.blocks_tensor(
+            cfg.seed, synth.T_V, blocks, b, cfg.hkv, cfg.d, cfg.dtype)))
+    return q, k_own, v_own, k_rest, v_rest, do
+
+
 def make_inputs(cfg, rank, layout="zigzag"):
     import torch
     from ring_attention_attn_amd import synth
     P, b = cfg.P, cfg.b
     blocks_of = synth.paired_blocks if layout == "zigzag" else synth.contiguous_blocks
     mine = blocks_of(P, rank)
-
-    def dev(bits):
-        if cfg.dtype == "bf16":
-            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(bits).cuda()
+    dev = lambda x: _dev(cfg, x)
 
     q = dev(synth.blocks_tensor(cfg.seed, synth.T_Q, mine, b, cfg.hq, cfg.d, cfg.dtype))
     do = dev(synth.blocks_tensor(cfg.seed, synth.T_DO, mine, b, cfg.hq, cfg.d, cfg.dtype))
@@ -82,6 +124,26 @@ def make_inputs(cfg, rank, layout="zigzag"):
         K.append(dev(synth.blocks_tensor(cfg.seed, synth.T_K, blocks, b, cfg.hkv, cfg.d, cfg.dtype)))
         V.append(dev(synth.blocks_tensor(cfg.seed, synth.T_V, blocks, b, cfg.hkv, cfg.d, cfg.dtype)))
     return q, torch.stack(K), torch.stack(V), do
+
+
+def cpu_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS numpy uses."""
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        pass
+    return model, blas
 
 
 def cpu_baseline(cfg, rank, budget_rows):
@@ -95,10 +157,10 @@ def cpu_baseline(cfg, rank, budget_rows):
     rows = np.linspace(0, 2 * b - 1, budget_rows).round().astype(np.int64)
     pos = oracle.zigzag_positions(cfg.S, P, rank)[rows]
     mine = synth.paired_blocks(P, rank)
-    q = synth.blocks_tensor(cfg.seed, synth.T_Q, mine, b, cfg.hq, cfg.d, cfg.dtype)[rows, :G]
-    do = synth.blocks_tensor(cfg.seed, synth.T_DO, mine, b, cfg.hq, cfg.d, cfg.dtype)[rows, :G]
-    k = synth.blocks_tensor(cfg.seed, synth.T_K, range(2 * P), b, cfg.hkv, cfg.d, cfg.dtype)[:, :1]
-    v = synth.blocks_tensor(cfg.seed, synth.T_V, range(2 * P), b, cfg.hkv, cfg.d, cfg.dtype)[:, :1]
+    q = synth.blocks_tensor(cfg.seed, synth.T_Q, mine, b, G, cfg.d, cfg.dtype)[rows]
+    do = synth.blocks_tensor(cfg.seed, synth.T_DO, mine, b, G, cfg.d, cfg.dtype)[rows]
+    k = synth.blocks_tensor(cfg.seed, synth.T_K, range(2 * P), b, 1, cfg.d, cfg.dtype)
+    v = synth.blocks_tensor(cfg.seed, synth.T_V, range(2 * P), b, 1, cfg.d, cfg.dtype)
     w = (lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)) if cfg.dtype == "bf16" else \
         (lambda a: a.astype(np.float64))
     q, do, k, v = w(q), w(do), w(k), w(v)
@@ -106,11 +168,42 @@ def cpu_baseline(cfg, rank, budget_rows):
     oracle.share_backward(q, k, v, do, pos, cfg.scale)
     dt = time.perf_counter() - t0
     flops = 14 * cfg.d * G * int(np.sum(pos + 1))
+    model, blas = cpu_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu": model, "blas": blas,
             "sample": (f"numpy fp64 oracle, fwd+bwd over the whole sequence for {budget_rows} of "
                        f"{2 * b} query rows (evenly spaced over both paired blocks) x {G} query "
-                       f"heads of one KV head; rank {rank}; cpu {platform.processor() or 'x86_64'}")}
+                       f"heads of one KV head; rank {rank}; BLAS threads = the cores available "
+                       f"({len(os.sched_getaffinity(0))})")}
+
+
+class EventTimer:
+    """HIP events around each library launch, on the stream the launches use."""
+
+    def __init__(self, stream):
+        import collections
+        self.stream = stream
+        self.ev = collections.defaultdict(list)
+
+    def __call__(self, kind):
+        import contextlib
+        import torch
+
+        @contextlib.contextmanager
+        def cm():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            yield
+            e1.record(self.stream)
+            self.ev[kind].append((e0, e1))
+        return cm()
+
+    def avg_ms(self, kind):
+        pairs = self.ev.get(kind, [])
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
+
+    def total_ms(self, kind):
+        return float(np.sum([a.elapsed_time(b) for a, b in self.ev.get(kind, [])]))
 
 
 def main():
@@ -143,17 +236,27 @@ def main():
     import torch
     from ring_attention_attn_amd import binding
     from ring_attention_attn_amd.configs import CONFIGS
-    from ring_attention_attn_amd.ring import ShareRing
+    from ring_attention_attn_amd.ring import HeadParallelShare, ShareRing
     binding.lib()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     cfg = CONFIGS[args.config]
+    wrapped = bool(cfg.permute_heads) and args.layout == "zigzag"
     log(f"config {cfg.name}: S={cfg.S} P={cfg.P} ({cfg.inner}x{cfg.outer}) hq={cfg.hq} "
-        f"hkv={cfg.hkv} d={cfg.d} {cfg.dtype} rank={args.rank}")
-    q, K, V, do = make_inputs(cfg, args.rank, args.layout)
-    ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d, cfg.dtype,
-                     merge=args.merge, layout=args.layout, kv_rings=args.kv_rings)
+        f"hkv={cfg.hkv} d={cfg.d} {cfg.dtype} rank={args.rank}"
+        + (f" head-parallel {cfg.hp} (head permutes in the step)" if wrapped else ""))
+    ring_kw = dict(merge=args.merge, layout=args.layout, kv_rings=args.kv_rings)
+    if wrapped:
+        inputs = make_head_parallel_inputs(cfg, args.rank)
+        share = HeadParallelShare(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq * cfg.hp,
+                                  cfg.hkv * cfg.hp, cfg.d, cfg.hp, group=0, dtype=cfg.dtype,
+                                  **ring_kw)
+        ring = share.ring
+    else:
+        inputs = make_inputs(cfg, args.rank, args.layout)
+        share = ring = ShareRing(cfg.S, cfg.inner, cfg.outer, args.rank, cfg.hq, cfg.hkv, cfg.d,
+                                 cfg.dtype, **ring_kw)
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(7)   # 1 GiB
         dst = torch.empty_like(src)
@@ -164,53 +267,21 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident; warmup")
     for _ in range(args.warmup):
-        ring.step(q, K, V, do)
+        share.step(*inputs)
     torch.cuda.synchronize()
     log("timed region")
 
     # per-launch HIP events on the stream the kernels run on (torch's current stream)
     stream = torch.cuda.current_stream()
-    ev = {"fwd": [], "bwd": [], "merge": []}
-    from ring_attention_attn_amd import binding as B
-
-    def timed_step():
-        for t, (j, off, desc) in enumerate(ring.launches):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            fused = t > 0 and args.merge == "fused"
-            o, l = (ring.o_acc, ring.lse_acc) if t == 0 or fused else (ring.o_step, ring.lse_step)
-            k, v = ring._kv(K, j, off), ring._kv(V, j, off)
-            e0.record(stream)
-            if fused:
-                B.ring_attn_step_fwd_merge(desc, q, k, v, o, l)
-            else:
-                B.ring_attn_step_fwd(desc, q, k, v, o, l)
-            e1.record(stream)
-            ev["fwd"].append((e0, e1))
-            if t > 0 and not fused:
-                m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                m0.record(stream)
-                B.lse_merge(ring.L, ring.hq, ring.d, ring.o_acc, ring.lse_acc, ring.o_step,
-                            ring.lse_step)
-                m1.record(stream)
-                ev["merge"].append((m0, m1))
-        B.ra_bwd_delta(ring.L, ring.hq, ring.d, B.RA_BF16 if cfg.dtype == "bf16" else B.RA_F32,
-                       ring.o_acc, do, ring.delta, ring.o_lowp if cfg.dtype == "bf16" else None)
-        B.ra_fill_f32(ring.dq, ring.dq.numel(), 0.0)
-        for j, off, desc in ring.launches:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            B.ring_attn_step_bwd(desc, q, ring._kv(K, j, off), ring._kv(V, j, off), do,
-                                 ring.lse_acc, ring.delta, ring.dq, ring._kv(ring.dk, j, off),
-                                 ring._kv(ring.dv, j, off))
-            e1.record(stream)
-            ev["bwd"].append((e0, e1))
-
+    timer = EventTimer(stream)
+    share.timer = timer
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        timed_step()
+    for _ in range(args.steps):
+        share.step(*inputs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    share.timer = None
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
     fwd_flops, bwd_flops = cfg.flops(args.layout, args.rank)
@@ -218,24 +289,26 @@ def main():
     ms = wall / args.steps * 1e3
     value = total * args.steps / wall / 1e12
 
-    def avg_ms(pairs):
-        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
-
+    from ring_attention_attn_amd import binding as B
     if args.merge == "fused":
         # the merge runs inside the forward launches; time the standalone kernel
-        # (outside the timed steps) for its own bandwidth figure
+        # (outside the timed steps, over all rows) for its own bandwidth figure
         ring.o_step.zero_()
         ring.lse_step.zero_()
+        mt = EventTimer(stream)
         for _ in range(6):
-            m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            m0.record(stream)
-            B.lse_merge(ring.L, ring.hq, ring.d, ring.o_acc, ring.lse_acc, ring.o_step,
-                        ring.lse_step)
-            m1.record(stream)
-            ev["merge"].append((m0, m1))
+            with mt("lse_merge"):
+                B.lse_merge(ring.L, ring.hq, ring.d, ring.o_acc, ring.lse_acc, ring.o_step,
+                            ring.lse_step)
         torch.cuda.synchronize()
-        ev["merge"] = ev["merge"][1:]
-    fwd_ms, bwd_ms, merge_ms = avg_ms(ev["fwd"]), avg_ms(ev["bwd"]), avg_ms(ev["merge"])
+        merge_ms = float(np.mean([a.elapsed_time(b) for a, b in mt.ev["lse_merge"][1:]]))
+        merge_rows = ring.L
+    else:
+        merge_ms = timer.avg_ms("lse_merge")
+        n_m = len(ring.launches) - 1
+        merge_rows = sum(ring.merge_rows(desc)[1] for _, _, desc in ring.launches[1:]) / max(n_m, 1)
+    fwd_ms, bwd_ms = timer.avg_ms("step_fwd"), timer.avg_ms("step_bwd")
+    delta_ms = timer.avg_ms("bwd_delta")
     # algorithmic flops per launch: each ring step carries 1/P of the share's pairs
     # (2b^2 per head per step, +b on the diagonal step); averaged over the P launches
     n_launch = len(ring.launches)   # P, or 2P with the block A / block B rings
@@ -243,7 +316,10 @@ def main():
     fwd_launch_flops = fwd_flops / n_launch
     bwd_tflops = bwd_launch_flops / (bwd_ms * 1e-3) / 1e12
     fwd_tflops = fwd_launch_flops / (fwd_ms * 1e-3) / 1e12
-    merge_bytes = cfg.rows * cfg.hq * (cfg.d * 4 * 3 + 4 * 3)
+    merge_bytes = merge_rows * cfg.hq * (cfg.d * 4 * 3 + 4 * 3)
+    # D = rowsum(dO O): reads O (fp32) and dO, writes O in bf16 and D
+    eb = 2 if cfg.dtype == "bf16" else 4
+    delta_bytes = ring.L * cfg.hq * (cfg.d * (4 + eb + (2 if cfg.dtype == "bf16" else 0)) + 4)
     out = {
         "metric": "ring-attention fwd+bwd TFLOP/s (causal-effective) and % bf16 MFMA peak, 1 GPU",
         "value": round(value, 2),
@@ -260,18 +336,28 @@ def main():
         "config": {"workload": cfg.name, "global_seq": cfg.S, "ring": f"{cfg.inner}x{cfg.outer}",
                    "local_rows": cfg.rows, "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.d,
                    "rank": args.rank, "layout": args.layout, "kv_rings": args.kv_rings,
+                   "head_parallel": cfg.hp, "head_permutes_in_step": wrapped,
                    "parallelism": "one GPU's share (virtual ring)"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "merge": args.merge,
         "breakdown_ms_per_launch": {"step_fwd": round(fwd_ms, 4), "step_bwd": round(bwd_ms, 4),
-                                    "lse_merge": round(merge_ms, 4)},
+                                    "lse_merge": round(merge_ms, 4),
+                                    "bwd_delta": round(delta_ms, 4)},
         "step_fwd_tflops": round(fwd_tflops, 1),
         "lse_merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms else None,
+        "bwd_delta_gbs": round(delta_bytes / (delta_ms * 1e-3) / 1e9, 1) if delta_ms else None,
         "roofline": {"bound": "mfma", "kernel": "ring_attn_step_bwd", "achieved": round(bwd_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(cfg.name)},
     }
+    util = recorded_mfma_util(cfg.name)
+    if util is not None:
+        out["mfma_busy_pct"] = util
+    if wrapped:
+        perm_ms = timer.total_ms("head_permute") / args.steps
+        out["breakdown_ms_per_step"] = {"head_permutes": round(perm_ms, 4)}
+        out["head_permute_gbs"] = round(share.permute_bytes() / (perm_ms * 1e-3) / 1e9, 1)
     if args.layout != "zigzag":
         log("cpu baseline is taken on the paired-block share only; skipped")
     elif not args.no_cpu_baseline:

@@ -123,6 +123,13 @@ ra_status ring_attn_step_fwd_merge(const ra_step_desc* desc, const void* q, cons
  * ring_attn_step_bwd -- one step's share of the attention gradient, driven by
  * the FINAL log-sum-exp and D of the rows (saved-LSE recompute).
  *
+ * The pages give no backward formula (the LoongTrain abstract only names
+ * Selective Checkpoint++ recomputation). The reading taken: the exact gradient
+ * of sum(dout * O) over this share's rows, restricted to the chunk's keys,
+ * with D from the final fp32 O; P and dS are rounded to bf16 (nearest even)
+ * before they enter a bf16 product, and dK/dV are this share's contribution
+ * only (a multi-GPU ring would sum them over the ranks).
+ *
  * P_ij = exp(s_ij - lse[h][i]) on visible pairs, dP_ij = dout_i . v_j,
  * dS_ij = P_ij (dP_ij - delta[h][i]);
  *   dq_acc[i][h]  += scale * sum_j dS_ij k_j          (always accumulates)
@@ -139,19 +146,27 @@ ra_status ring_attn_step_bwd(const ra_step_desc* desc, const void* q, const void
                              float* dv_acc, ra_stream_t stream);
 
 /*
- * lse_merge -- fold one step's partial result into the running one
- * (online-softmax rescaling of partial outputs over disjoint key sets):
+ * lse_merge -- fold one step's partial result into the running one: the
+ * "online-softmax rescaling" by which partial outputs over disjoint key sets
+ * are merged. The pages print no formula for it; this is the max-shifted
+ * log-sum-exp rescale (the reading taken):
  *   m = max(La, Ls); if m == -inf the row stays (O unchanged, L = -inf), else
  *   L = m + ln(e^(La-m) + e^(Ls-m)), O = e^(La-L) Oa + e^(Ls-L) Os.
  * o_acc, o_step: fp32 [rows][hq][d] contiguous; lse_acc, lse_step: fp32
- * [hq][rows]. o_acc and lse_acc are updated in place.
+ * [hq][rows]. Only rows [row_begin, row_begin + row_count) are read and
+ * updated (in place), e.g. the rows a ring step gave any visible key: with
+ * paired blocks, a chunk later than the rank's own is seen by block B only.
+ * RA_EINVAL unless 0 <= row_begin <= rows and 0 <= row_count <= rows - row_begin;
+ * row_count == 0 is a no-op.
  */
-ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, float* o_acc,
-                    float* lse_acc, const float* o_step, const float* lse_step,
-                    ra_stream_t stream);
+ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, int64_t row_begin,
+                    int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,
+                    const float* lse_step, ra_stream_t stream);
 
 /*
- * ra_bwd_delta -- backward preprocess of the merged forward result:
+ * ra_bwd_delta -- backward preprocess of the merged forward result. The pages
+ * give no formula; this is the row term of the exact softmax gradient (the same
+ * reading as ring_attn_step_bwd), computed from the final fp32 O:
  *   delta[h][i] = sum_x dout[i][h][x] * o[i][h][x]
  * and, if o_out != NULL, o_out = o rounded to bf16 (nearest even).
  * o: fp32 [rows][hq][d]; dout: dtype [rows][hq][d]; o_out: bf16 [rows][hq][d];

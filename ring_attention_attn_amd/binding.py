@@ -65,7 +65,7 @@ def lib():
             "ring_attn_step_fwd": [pd, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_fwd_merge": [pd, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_bwd": [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
-            "lse_merge": [i64, i32, i32, vp, vp, vp, vp, vp],
+            "lse_merge": [i64, i32, i32, i64, i64, vp, vp, vp, vp, vp],
             "ra_bwd_delta": [i64, i32, i32, i32, vp, vp, vp, vp, vp],
             "head_permute": [vp, vp, i64, i32, i32, i32, i32, i32, vp],
             "ra_fill_f32": [vp, i64, f32, vp],
@@ -183,13 +183,17 @@ def ring_attn_step_bwd(desc, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, 
                                     _ptr(dv_acc), _stream(stream)), "ring_attn_step_bwd")
 
 
-def lse_merge(rows, hq, head_dim, o_acc, lse_acc, o_step, lse_step, stream=None):
+def lse_merge(rows, hq, head_dim, o_acc, lse_acc, o_step, lse_step, stream=None, row_begin=0,
+              row_count=None):
+    """Merge rows [row_begin, row_begin + row_count) (default: all rows)."""
+    if row_count is None:
+        row_count = rows - row_begin
     if rows > 0 and hq > 0:
         for x, name, n in ((o_acc, "o_acc", rows * hq * head_dim), (o_step, "o_step", rows * hq * head_dim),
                            (lse_acc, "lse_acc", hq * rows), (lse_step, "lse_step", hq * rows)):
             _arg(x, name, 4 * n, "f32")
-    _check(lib().lse_merge(rows, hq, head_dim, _ptr(o_acc), _ptr(lse_acc), _ptr(o_step),
-                           _ptr(lse_step), _stream(stream)), "lse_merge")
+    _check(lib().lse_merge(rows, hq, head_dim, row_begin, row_count, _ptr(o_acc), _ptr(lse_acc),
+                           _ptr(o_step), _ptr(lse_step), _stream(stream)), "lse_merge")
 
 
 def ra_bwd_delta(rows, hq, head_dim, dtype, o, dout, delta, o_out=None, stream=None):

@@ -22,6 +22,9 @@ ra_status check_strides(int64_t ss, int64_t hs, int64_t rows, int32_t heads, int
   if (rows > 1 && heads > 1 && ss / heads < hs && hs / rows < ss) return RA_EINVAL;
   int64_t per16 = 16 / eb;
   if ((ss % per16) != 0 || (hs % per16) != 0) return RA_EALIGN;
+  // the kernels address a tile of up to 64 rows from its first row with 32-bit
+  // byte offsets (buffer loads), so 64 row strides must stay below 2^31 bytes
+  if (ss > ((int64_t)1 << 31) / (64 * eb) - 2 * d) return RA_EUNSUPPORTED;
   return RA_OK;
 }
 
@@ -162,16 +165,19 @@ ra_status ring_attn_step_bwd(const ra_step_desc* d, const void* q, const void* k
   return from_hip(launch_step_bwd(p, d->dtype, d->head_dim, (hipStream_t)stream));
 }
 
-ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, float* o_acc, float* lse_acc,
-                    const float* o_step, const float* lse_step, ra_stream_t stream) {
+ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, int64_t row_begin,
+                    int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,
+                    const float* lse_step, ra_stream_t stream) {
   if (rows < 0 || hq < 1) return RA_EINVAL;
+  if (row_begin < 0 || row_count < 0 || row_begin > rows || row_count > rows - row_begin)
+    return RA_EINVAL;
   if (head_dim != 64 && head_dim != 128) return RA_EUNSUPPORTED;
-  if (rows == 0) return RA_OK;
+  if (row_count == 0) return RA_OK;
   if (!o_acc || !lse_acc || !o_step || !lse_step) return RA_EINVAL;
   if (!aligned16(o_acc) || !aligned16(o_step) || !aligned16(lse_acc) || !aligned16(lse_step))
     return RA_EALIGN;
-  return from_hip(launch_lse_merge(rows, hq, head_dim, o_acc, lse_acc, o_step, lse_step,
-                                   (hipStream_t)stream));
+  return from_hip(launch_lse_merge(rows, hq, head_dim, row_begin, row_count, o_acc, lse_acc,
+                                   o_step, lse_step, (hipStream_t)stream));
 }
 
 ra_status ra_bwd_delta(int64_t rows, int32_t hq, int32_t head_dim, int32_t dtype, const float* o,

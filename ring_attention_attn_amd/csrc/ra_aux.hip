@@ -21,17 +21,20 @@ inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 1 << 20)
 // One thread per 4 consecutive floats of O; the D/4 threads of one (row, head)
 // vector sit in one wave, so every lane reads the old lse_acc before the one
 // lane that owns it stores the new value (in-order issue within a wave).
+// Only the rows [row_begin, row_begin + row_count) of the [rows][hq][d] tensors
+// are touched (the rows a ring step gave any visible key).
 template <int D>
 __global__ __launch_bounds__(kBlock) void lse_merge_kernel(int64_t rows, int32_t hq,
+                                                           int64_t row_begin, int64_t row_count,
                                                            float* __restrict__ o_acc,
                                                            float* __restrict__ lse_acc,
                                                            const float* __restrict__ o_step,
                                                            const float* __restrict__ lse_step) {
   constexpr int TPV = D / 4;  // threads per (row, head) vector
-  const int64_t nvec4 = rows * hq * TPV;
+  const int64_t nvec4 = row_count * hq * TPV;
   for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < nvec4;
        t += (int64_t)gridDim.x * kBlock) {
-    const int64_t vec = t / TPV;  // (row, head) pair, row-major
+    const int64_t vec = row_begin * hq + t / TPV;  // (row, head) pair, row-major
     const int x4 = (int)(t % TPV);
     const int64_t row = vec / hq;
     const int h = (int)(vec % hq);
@@ -133,16 +136,17 @@ __global__ __launch_bounds__(kBlock) void fill_kernel(float* __restrict__ dst, i
 
 }  // namespace
 
-hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, float* o_acc, float* lse_acc,
-                            const float* o_step, const float* lse_step, hipStream_t s) {
-  const int64_t work = rows * hq * (d / 4);
+hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, int64_t row_begin,
+                            int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,
+                            const float* lse_step, hipStream_t s) {
+  const int64_t work = row_count * hq * (d / 4);
   const unsigned g = grid_for(work, kBlock * 4, 8192);
   if (d == 128)
-    hipLaunchKernelGGL(lse_merge_kernel<128>, dim3(g), dim3(kBlock), 0, s, rows, hq, o_acc,
-                       lse_acc, o_step, lse_step);
+    hipLaunchKernelGGL(lse_merge_kernel<128>, dim3(g), dim3(kBlock), 0, s, rows, hq, row_begin,
+                       row_count, o_acc, lse_acc, o_step, lse_step);
   else
-    hipLaunchKernelGGL(lse_merge_kernel<64>, dim3(g), dim3(kBlock), 0, s, rows, hq, o_acc,
-                       lse_acc, o_step, lse_step);
+    hipLaunchKernelGGL(lse_merge_kernel<64>, dim3(g), dim3(kBlock), 0, s, rows, hq, row_begin,
+                       row_count, o_acc, lse_acc, o_step, lse_step);
   return hipGetLastError();
 }
 

@@ -61,8 +61,9 @@ struct StepParams {
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_step_fwd(const StepParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_step_bwd(const StepParams& p, int dtype, int head_dim, hipStream_t s);
-hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, float* o_acc, float* lse_acc,
-                            const float* o_step, const float* lse_step, hipStream_t s);
+hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, int64_t row_begin,
+                            int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,
+                            const float* lse_step, hipStream_t s);
 hipError_t launch_bwd_delta(int64_t rows, int32_t hq, int32_t d, int32_t dtype, const float* o,
                             const void* dout, float* delta, void* o_out, hipStream_t s);
 hipError_t launch_head_permute(const void* src, void* dst, int64_t s, int32_t h, int32_t d,

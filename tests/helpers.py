@@ -1,4 +1,13 @@
-"""Shared test helpers: seeded share inputs (numpy + device), error reports."""
+"""Shared test helpers: seeded share inputs (numpy + device), error reports.
+
+Every GPU-vs-oracle comparison made through :func:`assert_close` is appended,
+with its test id, error and bar, to the JSON-lines file named by the
+RA_PARITY_LOG environment variable (if set), so that the margins of a run can
+be tabulated (tests/parity_margins.py).
+"""
+import json
+import os
+
 import numpy as np
 
 from ring_attention_attn_amd import synth
@@ -19,12 +28,13 @@ def share_inputs(S, P, r, hq, hkv, d, dtype, seed, layout="zigzag"):
     k_nat = synth.blocks_tensor(seed, synth.T_K, range(2 * P), b, hkv, d, dtype)
     v_nat = synth.blocks_tensor(seed, synth.T_V, range(2 * P), b, hkv, d, dtype)
 
-    def chunk(nat, j):
-        return np.concatenate([nat[blk * b:(blk + 1) * b] for blk in blocks_of(P, j)])
+    # chunk j = its blocks in order, gathered in one copy per tensor
+    idx = np.array([blocks_of(P, j) for j in range(P)])
 
-    k_ch = np.stack([chunk(k_nat, j) for j in range(P)])
-    v_ch = np.stack([chunk(v_nat, j) for j in range(P)])
-    return dict(q=q, do=do, k_nat=k_nat, v_nat=v_nat, k_ch=k_ch, v_ch=v_ch, b=b)
+    def chunks(nat):
+        return nat.reshape(2 * P, b, hkv, d)[idx].reshape(P, 2 * b, hkv, d)
+
+    return dict(q=q, do=do, k_nat=k_nat, v_nat=v_nat, k_ch=chunks(k_nat), v_ch=chunks(v_nat), b=b)
 
 
 def widen(x, dtype):
@@ -63,11 +73,25 @@ TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
 REL_L2_BAR = 1e-2   # non-triviality check beside the absolute bar (bf16)
 
 
+CURRENT_TEST = None   # set per test by tests/conftest.py
+
+
+def _record(name, dtype, is_lse, err, atol, rl):
+    path = os.environ.get("RA_PARITY_LOG")
+    if not path:
+        return
+    rec = dict(test=CURRENT_TEST, tensor=name, dtype=dtype, kind="lse" if is_lse else "value",
+               max_abs=err, bar=atol, rel_l2=rl)
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
+
+
 def assert_close(name, got, want, dtype, is_lse=False):
     atol = TOL[dtype][1 if is_lse else 0]
     err = max_abs(got, want)
+    rl = rel_l2(got, want) if not is_lse else None
+    _record(name, dtype, is_lse, err, atol, rl)
     assert err <= atol, f"{name}: max abs err {err:.3e} > {atol:.1e}"
     if dtype == "bf16" and not is_lse:
-        rl = rel_l2(got, want)
         assert rl <= REL_L2_BAR, f"{name}: rel L2 {rl:.3e} > {REL_L2_BAR:.0e}"
     return err

@@ -79,9 +79,14 @@ def test_validation_accepts_good_descriptor():
     assert B.ra_validate_step(good_desc(), 1) == B.RA_OK
     # head-major layout is a valid nesting too
     assert B.ra_validate_step(good_desc(q_strides=(128, 128 * 128), o_strides=(128, 128 * 128)), 0) == B.RA_OK
-    # very large (padded) strides in either nesting
-    assert B.ra_validate_step(good_desc(q_strides=(2**62, 128)), 0) == B.RA_OK
+    # padded strides in either nesting; any head stride
+    assert B.ra_validate_step(good_desc(q_strides=(1024 + 64, 128)), 0) == B.RA_OK
     assert B.ra_validate_step(good_desc(q_strides=(128, 2**62)), 0) == B.RA_OK
+    # the largest row stride whose 64-row tile stays within 32-bit byte offsets
+    big = 2**31 // 128 - 256
+    assert B.ra_validate_step(good_desc(q_strides=(big, 128)), 0) == B.RA_OK
+    assert B.ra_validate_step(good_desc(q_strides=(big + 8, 128)), 0) == B.RA_EUNSUPPORTED
+    assert B.ra_validate_step(good_desc(q_strides=(2**62, 128)), 0) == B.RA_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -141,6 +146,9 @@ def test_calls_reject_before_device_work():
         (lambda: B.lse_merge(-1, 4, 128, 16, 16, 16, 16, stream=0), B.RA_EINVAL),
         (lambda: B.lse_merge(8, 4, 80, 16, 16, 16, 16, stream=0), B.RA_EUNSUPPORTED),
         (lambda: B.lse_merge(8, 4, 128, 16, 16, 16, 8, stream=0), B.RA_EALIGN),
+        (lambda: B.lse_merge(8, 4, 128, 16, 16, 16, 16, stream=0, row_begin=-1), B.RA_EINVAL),
+        (lambda: B.lse_merge(8, 4, 128, 16, 16, 16, 16, stream=0, row_begin=4, row_count=5),
+         B.RA_EINVAL),                                                   # past the last row
         (lambda: B.ra_bwd_delta(8, 4, 128, 5, 16, 16, 16, stream=0), B.RA_EINVAL),
         (lambda: B.head_permute(16, 4096, 8, 6, 128, 4, 2, stream=0), B.RA_EINVAL),   # H % P
         (lambda: B.head_permute(16, 4096, 8, 8, 4, 8, 2, stream=0), B.RA_EALIGN),     # 8-byte runs
@@ -156,6 +164,7 @@ def test_calls_reject_before_device_work():
 
 def test_zero_size_calls_are_noops():
     B.lse_merge(0, 4, 128, 0, 0, 0, 0, stream=0)
+    B.lse_merge(8, 4, 128, 0, 0, 0, 0, stream=0, row_begin=8, row_count=0)
     B.ra_fill_f32(0, 0, 1.0, stream=0)
     B.head_permute(0, 0, 0, 8, 128, 4, 2, stream=0)
     B.ring_attn_step_fwd(good_desc(q_segments=((0, 448), 0)), 0, 0, 0, 0, 0, stream=0)
@@ -194,3 +203,28 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(B.RaError) as e:
         B.ring_attn_step_fwd(good_desc(head_dim=96), q, k, k, o, lse, stream=0)
     assert e.value.status == B.RA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("layout,S,inner,outer,r", [("zigzag", 512, 4, 1, 1), ("zigzag", 4096, 4, 2, 6),
+                                                     ("contiguous", 512, 4, 1, 2)])
+@pytest.mark.parametrize("kv_rings", ["one", "ab"])
+def test_ring_merge_rows_are_the_rows_that_see_a_key(layout, S, inner, outer, r, kv_rings):
+    """The separate merge's row range of each launch: exactly the query rows
+    with a visible key in the launch's key set (host logic of the ring driver)."""
+    from ring_attention_attn_amd.ring import ShareRing
+    if layout == "contiguous" and kv_rings == "ab":
+        return
+    P = inner * outer
+    ring = ShareRing(S, inner, outer, r, 1, 1, 64, "f32", device="cpu", merge="separate",
+                     layout=layout, kv_rings=kv_rings)
+    posf = oracle.zigzag_positions if layout == "zigzag" else oracle.contiguous_positions
+    pos_q = posf(S, P, r)
+    for j, off, desc in ring.launches:
+        pos_k = posf(S, P, j)
+        n = desc.k_nseg * desc.k_seg_len
+        pos_k = pos_k[off:off + n]
+        sees = (pos_q[:, None] >= pos_k[None, :]).any(axis=1)
+        r0, cnt = ring.merge_rows(desc)
+        want = np.zeros(len(pos_q), bool)
+        want[r0:r0 + cnt] = True
+        assert np.array_equal(sees, want), (j, off)

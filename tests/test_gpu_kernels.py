@@ -29,6 +29,46 @@ def B():
     return binding
 
 
+# ------------------------------------------------------------------ guard bands
+# Every output of a call under test sits inside a larger buffer, with guard
+# bands of a fixed bit pattern before and after it; a write past either end of
+# an output changes a band.
+GUARD = 4096                       # elements on each side
+_PATTERN = {torch.float32: (torch.int32, 0x5A5A5A5A), torch.bfloat16: (torch.int16, 0x5A5A),
+            torch.int16: (torch.int16, 0x5A5A), torch.int32: (torch.int32, 0x5A5A5A5A)}
+_guarded = []                      # (buffer, n) of the current test
+
+
+def guarded(shape, dtype=torch.float32, fill=float("nan")):
+    """A contiguous tensor of ``shape`` between two guard bands."""
+    n = int(np.prod(shape))
+    buf = torch.empty(n + 2 * GUARD, dtype=dtype, device="cuda")
+    idt, pat = _PATTERN[dtype]
+    buf.view(idt).fill_(pat)
+    t = buf[GUARD:GUARD + n].view(shape)
+    if fill is not None:
+        t.fill_(fill)
+    _guarded.append((buf, n))
+    return t
+
+
+def check_guards():
+    torch.cuda.synchronize()
+    for buf, n in _guarded:
+        idt, pat = _PATTERN[buf.dtype]
+        ib = buf.view(idt)
+        assert bool((ib[:GUARD] == pat).all()), "write before the start of an output"
+        assert bool((ib[GUARD + n:] == pat).all()), "write past the end of an output"
+    _guarded.clear()
+
+
+@pytest.fixture(autouse=True)
+def _guards_checked():
+    _guarded.clear()
+    yield
+    check_guards()
+
+
 # ------------------------------------------------------------------ head permute
 
 @pytest.mark.parametrize("s,h,d,p,eb", [(37, 8, 128, 4, 2), (64, 32, 128, 4, 2), (5, 6, 16, 3, 4),
@@ -39,9 +79,9 @@ def test_head_permute_bit_exact(s, h, d, p, eb):
     x = rng.integers(0, np.iinfo(dt).max, size=(s, h, d), dtype=dt)
     tdt = torch.int16 if eb == 2 else torch.int32
     src = torch.from_numpy(x.view(np.int16 if eb == 2 else np.int32)).cuda()
-    dst = torch.empty((p, s, h // p, d), dtype=tdt, device="cuda")
+    dst = guarded((p, s, h // p, d), tdt, fill=None)
     B().head_permute(src, dst, s, h, d, p, eb, 0)
-    back = torch.empty_like(src)
+    back = guarded((s, h, d), tdt, fill=None)
     B().head_permute(dst, back, s, h, d, p, eb, 1)
     torch.cuda.synchronize()
     want = oracle.head_permute(x, p)
@@ -53,7 +93,7 @@ def test_head_permute_full_size_2d_attention_share():
     """The 2D-Attention share's permute: 65,536 tokens x 32 heads x 128 bf16 into
     4 head groups (and back), bit-exact."""
     s, h, d, p = 65536, 32, 128, 4
-    x = synth.blocks_tensor(1003, synth.T_QPRE, [0], s, h, d, "bf16")
+    x = synth.blocks_tensor(1003, synth.T_Q, [0], s, h, d, "bf16")
     src = torch.from_numpy(x.view(np.int16)).cuda()
     dst = torch.empty((p, s, h // p, d), dtype=torch.int16, device="cuda")
     B().head_permute(src, dst, s, h, d, p, 2, 0)
@@ -80,6 +120,10 @@ def test_lse_merge(rows, hq, d):
     os_[::7] = 0.0
     want_o, want_l = oracle.lse_merge(oa, la, os_, ls)
     t = [torch.from_numpy(a.copy()).cuda() for a in (oa, la, os_, ls)]
+    for i in (0, 1):
+        g = guarded(t[i].shape, fill=None)
+        g.copy_(t[i])
+        t[i] = g
     B().lse_merge(rows, hq, d, t[0], t[1], t[2], t[3])
     torch.cuda.synchronize()
     got_o, got_l = t[0].cpu().numpy(), t[1].cpu().numpy()
@@ -87,6 +131,29 @@ def test_lse_merge(rows, hq, d):
     assert np.array_equal(np.isneginf(got_l), np.isneginf(want_l))
     assert max_abs(got_o, want_o) < 2e-6
     assert max_abs(got_l, want_l) < 2e-6
+
+
+def test_lse_merge_row_range():
+    """Only rows [row_begin, row_begin + row_count) are merged; every other row
+    of O and LSE keeps its bits."""
+    rows, hq, d, r0, n = 300, 4, 128, 117, 90
+    rng = np.random.default_rng(5)
+    oa, os_ = (rng.standard_normal((rows, hq, d)).astype(np.float32) for _ in range(2))
+    la, ls = ((rng.standard_normal((hq, rows)) * 2).astype(np.float32) for _ in range(2))
+    want_o, want_l = oracle.lse_merge(oa, la, os_, ls)
+    to, tl = guarded((rows, hq, d), fill=None), guarded((hq, rows), fill=None)
+    to.copy_(torch.from_numpy(oa))
+    tl.copy_(torch.from_numpy(la))
+    B().lse_merge(rows, hq, d, to, tl, torch.from_numpy(os_).cuda(), torch.from_numpy(ls).cuda(),
+                  row_begin=r0, row_count=n)
+    torch.cuda.synchronize()
+    go, gl = to.cpu().numpy(), tl.cpu().numpy()
+    inside = slice(r0, r0 + n)
+    assert max_abs(go[inside], want_o[inside]) < 2e-6
+    assert max_abs(gl[:, inside], want_l[:, inside]) < 2e-6
+    for outside in (slice(0, r0), slice(r0 + n, rows)):
+        assert np.array_equal(go[outside], oa[outside])
+        assert np.array_equal(gl[:, outside], la[:, outside])
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
@@ -98,8 +165,8 @@ def test_bwd_delta_and_cast(dtype, d):
     want = np.einsum("lhd,lhd->hl", widen(g, dtype), o.astype(np.float64))
     to = torch.from_numpy(o).cuda()
     tg = to_device(g, dtype)
-    delta = torch.empty((hq, rows), dtype=torch.float32, device="cuda")
-    ob = torch.empty((rows, hq, d), dtype=torch.bfloat16, device="cuda")
+    delta = guarded((hq, rows))
+    ob = guarded((rows, hq, d), torch.bfloat16)
     B().ra_bwd_delta(rows, hq, d, B().RA_BF16 if dtype == "bf16" else B().RA_F32, to, tg, delta, ob)
     torch.cuda.synchronize()
     assert max_abs(delta.cpu().numpy(), want) < 1e-4
@@ -108,7 +175,7 @@ def test_bwd_delta_and_cast(dtype, d):
 
 
 def test_fill():
-    x = torch.empty(1000003, dtype=torch.float32, device="cuda")
+    x = guarded((1000003,))
     B().ra_fill_f32(x, x.numel(), -2.5)
     torch.cuda.synchronize()
     assert bool((x == -2.5).all())
@@ -159,10 +226,14 @@ def test_step_forward(case):
     kc = to_device(x["k_ch"], dtype)
     vc = to_device(x["v_ch"], dtype)
     for j in range(P):
-        o = torch.full((L, hq, d), float("nan"), device="cuda")
-        lse = torch.full((hq, L), float("nan"), device="cuda")
-        B().ring_attn_step_fwd(_desc(dtype, d, hq, hkv, S, P, r, j, causal), q, kc[j], vc[j], o, lse)
+        o = guarded((L, hq, d))
+        lse = guarded((hq, L))
+        desc = _desc(dtype, d, hq, hkv, S, P, r, j, causal)
+        B().ring_attn_step_fwd(desc, q, kc[j], vc[j], o, lse)
+        o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+        B().ring_attn_step_fwd(desc, q, kc[j], vc[j], o2, lse2)
         torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), f"chunk {j}: not deterministic"
         want_o, want_l = _oracle_step_fwd(x, S, P, r, j, d, dtype, causal)
         got_l = lse.cpu().numpy()
         assert np.array_equal(np.isneginf(got_l), np.isneginf(want_l)), f"chunk {j}: empty rows"
@@ -223,8 +294,8 @@ def test_step_forward_merge(case):
     q = to_device(x["q"], dtype)
     kc = to_device(x["k_ch"], dtype)
     vc = to_device(x["v_ch"], dtype)
-    o_f = torch.zeros((L, hq, d), device="cuda")
-    l_f = torch.full((hq, L), float("-inf"), device="cuda")
+    o_f = guarded((L, hq, d), fill=0.0)
+    l_f = guarded((hq, L), fill=float("-inf"))
     o_u = torch.zeros((L, hq, d), device="cuda")
     l_u = torch.full((hq, L), float("-inf"), device="cuda")
     o_s = torch.empty((L, hq, d), device="cuda")
@@ -274,12 +345,18 @@ def test_step_backward(case):
         want_dq, want_dk, want_dv = oracle.step_backward(
             q64, widen(x["k_ch"][j], dtype), widen(x["v_ch"][j], dtype), do64, full["LSE"],
             full["D"], pos_q, pos_k, scale)
-        dq = torch.zeros((L, hq, d), device="cuda")
-        dk = torch.full((L, hkv, d), float("nan"), device="cuda")
-        dv = torch.full((L, hkv, d), float("nan"), device="cuda")
-        B().ring_attn_step_bwd(_desc(dtype, d, hq, hkv, S, P, r, j, causal), q, kc[j], vc[j], do,
-                               lse, delta, dq, dk, dv)
+        dq = guarded((L, hq, d), fill=0.0)
+        dk = guarded((L, hkv, d))
+        dv = guarded((L, hkv, d))
+        desc = _desc(dtype, d, hq, hkv, S, P, r, j, causal)
+        B().ring_attn_step_bwd(desc, q, kc[j], vc[j], do, lse, delta, dq, dk, dv)
+        # deterministic: a second run from the same state gives the same bits
+        dq2 = torch.zeros_like(dq)
+        dk2, dv2 = torch.full_like(dk, float("nan")), torch.full_like(dv, float("nan"))
+        B().ring_attn_step_bwd(desc, q, kc[j], vc[j], do, lse, delta, dq2, dk2, dv2)
         torch.cuda.synchronize()
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), \
+            f"chunk {j}: backward not deterministic"
         assert_close(f"dQ chunk {j}", dq.cpu().numpy(), want_dq, dtype)
         assert_close(f"dK chunk {j}", dk.cpu().numpy(), want_dk, dtype)
         assert_close(f"dV chunk {j}", dv.cpu().numpy(), want_dv, dtype)
@@ -290,3 +367,73 @@ def test_step_backward(case):
                                vc[j], do, lse, delta, dq, dk, dv)
         torch.cuda.synchronize()
         assert torch.equal(dk, 2 * dk1) and torch.equal(dv, 2 * dv1), f"accumulate chunk {j}"
+
+
+# ------------------------------------------------------------------ strided layouts
+
+def _in_layout(x_dev, layout, pad=64):
+    """A [L][H][d] device tensor copied into a buffer of another layout; returns
+    (buffer, (seq stride, head stride), view of the buffer as [L][H][d])."""
+    L, H, d = x_dev.shape
+    if layout == "padded_rows":          # [L][H*d + pad]
+        buf = torch.zeros((L, H * d + pad), dtype=x_dev.dtype, device="cuda")
+        view = buf.as_strided((L, H, d), (H * d + pad, d, 1))
+        strides = (H * d + pad, d)
+    elif layout == "head_major":         # [H][L][d]
+        buf = torch.zeros((H, L, d), dtype=x_dev.dtype, device="cuda")
+        view = buf.permute(1, 0, 2)
+        strides = (d, L * d)
+    elif layout == "padded_heads":       # [L][H][d + 32]
+        buf = torch.zeros((L, H, d + 32), dtype=x_dev.dtype, device="cuda")
+        view = buf[:, :, :d]
+        strides = (H * (d + 32), d + 32)
+    else:
+        raise ValueError(layout)
+    view.copy_(x_dev)
+    return buf, strides, view
+
+
+@pytest.mark.parametrize("layout", ["padded_rows", "head_major", "padded_heads"])
+def test_step_strided_layouts(layout):
+    """The descriptor's strides are honoured: forward and backward of a ring step
+    with every tensor in a padded or head-major layout, against the oracle."""
+    dtype, d, hq, hkv, b, P, r, j = "bf16", 128, 8, 2, 200, 4, 2, 1
+    S, L = 2 * P * b, 2 * b
+    scale = 1 / math.sqrt(d)
+    x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=81)
+    pos_q = oracle.zigzag_positions(S, P, r)
+    pos_k = oracle.zigzag_positions(S, P, j)
+    q64, do64 = widen(x["q"], dtype), widen(x["do"], dtype)
+    k64, v64 = widen(x["k_ch"][j], dtype), widen(x["v_ch"][j], dtype)
+    full = oracle.share_backward(q64, widen(x["k_nat"], dtype), widen(x["v_nat"], dtype), do64,
+                                 pos_q, scale)
+    want_o, want_l = oracle.step_forward(q64, k64, v64, pos_q, pos_k, scale)
+    want_dq, want_dk, want_dv = oracle.step_backward(q64, k64, v64, do64, full["LSE"], full["D"],
+                                                     pos_q, pos_k, scale)
+    q, qs, _ = _in_layout(to_device(x["q"], dtype), layout)
+    k, ks, _ = _in_layout(to_device(x["k_ch"][j], dtype), layout)
+    v, vs, _ = _in_layout(to_device(x["v_ch"][j], dtype), layout)
+    do, dos, _ = _in_layout(to_device(x["do"], dtype), layout)
+    o, os_, o_view = _in_layout(torch.full((L, hq, d), float("nan"), device="cuda"), layout)
+    dq, _, dq_view = _in_layout(torch.zeros((L, hq, d), device="cuda"), layout)
+    dk, dks, dk_view = _in_layout(torch.full((L, hkv, d), float("nan"), device="cuda"), layout)
+    dv, _, dv_view = _in_layout(torch.full((L, hkv, d), float("nan"), device="cuda"), layout)
+    (qp, _), (kp, _) = B().ra_zigzag_segments(S, P, r), B().ra_zigzag_segments(S, P, j)
+    desc = B().make_desc(dtype=B().RA_BF16, head_dim=d, hq=hq, hkv=hkv, q_segments=(qp, b),
+                         k_segments=(kp, b), scale=scale, q_strides=qs, k_strides=ks,
+                         v_strides=vs, o_strides=os_, do_strides=dos, dk_strides=dks)
+    lse = torch.empty((hq, L), device="cuda")
+    B().ring_attn_step_fwd(desc, q, k, v, o, lse)
+    lse_f = torch.from_numpy(np.ascontiguousarray(full["LSE"], dtype=np.float32)).cuda()
+    delta = torch.from_numpy(np.ascontiguousarray(full["D"], dtype=np.float32)).cuda()
+    B().ring_attn_step_bwd(desc, q, k, v, do, lse_f, delta, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert_close("O", o_view.cpu().numpy(), want_o, dtype)
+    assert_close("LSE", lse.cpu().numpy(), want_l, dtype, is_lse=True)
+    assert_close("dQ", dq_view.cpu().numpy(), want_dq, dtype)
+    assert_close("dK", dk_view.cpu().numpy(), want_dk, dtype)
+    assert_close("dV", dv_view.cpu().numpy(), want_dv, dtype)
+    if layout != "head_major":
+        # the padding is never written
+        pad_o = o.view(L, -1)[:, hq * d:] if layout == "padded_rows" else o[:, :, d:]
+        assert bool((pad_o == 0).all())

@@ -165,50 +165,149 @@ def test_ring_order_invariance():
     assert max_abs(o1.cpu().numpy(), o2.cpu().numpy()) < 1e-5
 
 
+HP_CASES = [
+    # name, S, inner, outer, rank, H, Hkv, d, hp, group
+    ("hp4_gqa4_2x2_g2", 4096, 2, 2, 1, 16, 4, 128, 4, 2),
+    ("hp2_gqa2_ragged_d64_g1", 1600, 4, 1, 3, 8, 4, 64, 2, 1),
+    ("hp4_mha_g0", 2048, 4, 1, 0, 8, 8, 128, 4, 0),
+]
+
+
+def head_parallel_inputs(S, P, r, H, Hkv, d, hp, g, seed):
+    """All-head Q/dO of the rank's rows, all-KV-head K/V of its own chunk, and
+    the other chunks' K/V in head-group g layout (as the ring would deliver
+    them); plus the oracle's view of head group g (natural-order K/V)."""
+    from ring_attention_attn_amd import synth
+    b = S // (2 * P)
+    hq, hkv = H // hp, Hkv // hp
+    gk = range(g * hkv, (g + 1) * hkv)
+    mine = synth.paired_blocks(P, r)
+    x = dict(b=b)
+    x["q_full"] = synth.blocks_tensor(seed, synth.T_Q, mine, b, H, d, "bf16")
+    x["do_full"] = synth.blocks_tensor(seed, synth.T_DO, mine, b, H, d, "bf16")
+    x["k_own"] = synth.blocks_tensor(seed, synth.T_K, mine, b, Hkv, d, "bf16")
+    x["v_own"] = synth.blocks_tensor(seed, synth.T_V, mine, b, Hkv, d, "bf16")
+    x["k_rest"] = [None if j == r else synth.blocks_tensor(seed, synth.T_K, synth.paired_blocks(P, j),
+                                                           b, gk, d, "bf16") for j in range(P)]
+    x["v_rest"] = [None if j == r else synth.blocks_tensor(seed, synth.T_V, synth.paired_blocks(P, j),
+                                                           b, gk, d, "bf16") for j in range(P)]
+    x["k_nat"] = synth.blocks_tensor(seed, synth.T_K, range(2 * P), b, gk, d, "bf16")
+    x["v_nat"] = synth.blocks_tensor(seed, synth.T_V, range(2 * P), b, gk, d, "bf16")
+    x["q"] = x["q_full"][:, g * hq:(g + 1) * hq]
+    x["do"] = x["do_full"][:, g * hq:(g + 1) * hq]
+    return x
+
+
+def run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x, sentinel=7.25):
+    """The 2D-Attention share through HeadParallelShare. Exchange slots other
+    than g are filled with ``sentinel`` first: they stand for the other
+    head-parallel ranks' data and must come back bit for bit."""
+    from ring_attention_attn_amd.ring import HeadParallelShare
+    hp_share = HeadParallelShare(S, inner, outer, r, H, Hkv, d, hp, group=g)
+    for t in (hp_share.o_x, hp_share.dq_x, hp_share.dk_x, hp_share.dv_x):
+        t.fill_(sentinel)
+    dev = lambda a: to_device(a, "bf16")
+    k_rest = [None if a is None else dev(a) for a in x["k_rest"]]
+    v_rest = [None if a is None else dev(a) for a in x["v_rest"]]
+    o, lse = hp_share.forward(dev(x["q_full"]), dev(x["k_own"]), dev(x["v_own"]), k_rest, v_rest)
+    dq, dk_own, dv_own = hp_share.backward(dev(x["do_full"]))
+    torch.cuda.synchronize()
+    hq, hkv = H // hp, Hkv // hp
+    P = inner * outer
+    got = dict(O_full=o.cpu().numpy(), LSE=lse.cpu().numpy(), dQ_full=dq.cpu().numpy(),
+               dK_own=dk_own.cpu().numpy(), dV_own=dv_own.cpu().numpy())
+    got["O"] = got["O_full"][:, g * hq:(g + 1) * hq]
+    got["dQ"] = got["dQ_full"][:, g * hq:(g + 1) * hq]
+    # per-chunk dK/dV of this head group, in the chunk order of the ring buffers
+    got["dK"] = np.stack([got["dK_own"][:, g * hkv:(g + 1) * hkv] if j == r else
+                          hp_share.dk_chunks[j].cpu().numpy() for j in range(P)])
+    got["dV"] = np.stack([got["dV_own"][:, g * hkv:(g + 1) * hkv] if j == r else
+                          hp_share.dv_chunks[j].cpu().numpy() for j in range(P)])
+    other_q = np.ones(H, bool)
+    other_q[g * hq:(g + 1) * hq] = False
+    other_k = np.ones(Hkv, bool)
+    other_k[g * hkv:(g + 1) * hkv] = False
+    for name, arr, mask in (("O", got["O_full"], other_q), ("dQ", got["dQ_full"], other_q),
+                            ("dK", got["dK_own"], other_k), ("dV", got["dV_own"], other_k)):
+        assert bool((arr[:, mask] == np.float32(sentinel)).all()), \
+            f"{name}: the other head groups' slots were not carried through unchanged"
+    return hp_share, got
+
+
+@pytest.mark.parametrize("case", HP_CASES, ids=lambda c: c[0])
+def test_head_parallel_share_matches_oracle(case):
+    """2D-Attention: head permute of Q/dO and of the own K/V chunk, the ring on
+    head group g, inverse permute of O/dQ and of the own chunk's dK/dV. Outputs
+    in the all-head layout against the oracle on the full-head tensors
+    restricted to group g (query head h uses KV head h div (H/Hkv) throughout)."""
+    name, S, inner, outer, r, H, Hkv, d, hp, g = case
+    P = inner * outer
+    x = head_parallel_inputs(S, P, r, H, Hkv, d, hp, g, seed=6000 + S + r)
+    _, got = run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x)
+    pos = oracle.zigzag_positions(S, P, r)
+    w = lambda a: widen(a, "bf16")
+    want = oracle.share_backward(w(x["q"]), w(x["k_nat"]), w(x["v_nat"]), w(x["do"]), pos,
+                                 1 / math.sqrt(d))
+    assert_close("O", got["O"], want["O"], "bf16")
+    assert_close("LSE", got["LSE"], want["LSE"], "bf16", is_lse=True)
+    assert_close("dQ", got["dQ"], want["dQ"], "bf16")
+    for j in range(P):
+        kp = oracle.zigzag_positions(S, P, j)
+        assert_close(f"dK[{j}]", got["dK"][j], want["dK"][kp], "bf16")
+        assert_close(f"dV[{j}]", got["dV"][j], want["dV"][kp], "bf16")
+
+
 def _sample_rows(b, n_rand, seed):
     fixed = [0, 1, 31, 32, 63, 64, 127, b - 1, b, b + 1, b + 63, 2 * b - 64, 2 * b - 1]
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([fixed, rng.integers(0, 2 * b, n_rand)]))
 
 
+def _sample_keys(b, seed):
+    """Key rows of a chunk: both blocks, the 32- and 128-key workgroup edges,
+    the first and last rows, and a few random ones."""
+    fixed = [0, 1, 31, 32, 127, 128, b - 1, b, b + 1, b + 127, b + 128, 2 * b - 1]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([fixed, rng.integers(0, 2 * b, 4)]))
+
+
 FULL_SIZE = ["llama3_8b_cp8_128k", "llama3_70b_hp2_cp32_512k", "hp4_cp16_1m", "mha7b_hp8_cp8_1m"]
+FULL_CASES = [(c, rank) for c in FULL_SIZE for rank in ("first", "last")]
 
 
-@pytest.mark.parametrize("cfg_name", FULL_SIZE)
-def test_full_size_share_sampled(cfg_name):
-    """Each bf16 workload at full size, in the benchmark's launch configuration.
+@pytest.mark.parametrize("cfg_name,which", FULL_CASES, ids=lambda v: str(v))
+def test_full_size_share_sampled(cfg_name, which):
+    """Each bf16 workload at full size, in the benchmark's launch configuration,
+    for the first and the last ring rank.
 
-    Sampled query rows (both zigzag halves, tile edges) of several heads: O, LSE
-    and dQ from the oracle row by row. Sampled late keys (the last 64 positions,
-    seen only by this rank's last rows): dK and dV from the oracle. Identities
-    over all keys: sum_k dV_k = sum of dO over the group's rows and heads, and
-    sum_k dK_k = 0. For the 2D-Attention workload the local queries come from
-    the head permute of a [rows][32][128] tensor (destination group 0), as the
-    head-parallel all-to-all would deliver them."""
-    from ring_attention_attn_amd import binding as B
-    from ring_attention_attn_amd import synth
+    Sampled query rows (both zigzag halves, tile edges) of several heads: O,
+    LSE, D and dQ from the oracle row by row. Sampled keys of chunks 0, 1 and
+    P-1 (both blocks, workgroup edges): dK and dV from the oracle over every
+    local row, driven by the GPU's final LSE and D (which the row samples pin).
+    Identities over all keys: sum_k dV_k = sum of dO over the group's rows and
+    heads, and sum_k dK_k = 0. The 2D-Attention workload runs through the head
+    permutes (all-head inputs and outputs, head group 0). The 128K workload
+    also runs its backward a second time and must give the same bits."""
     cfg = CONFIGS[cfg_name]
-    S, P, r, hq, hkv, d = cfg.S, cfg.P, 0, cfg.hq, cfg.hkv, cfg.d
+    S, P, hq, hkv, d = cfg.S, cfg.P, cfg.hq, cfg.hkv, cfg.d
+    r = 0 if which == "first" else P - 1
     G = hq // hkv
     scale = 1 / math.sqrt(d)
-    print(f"[full-size] {cfg_name}: S={S} P={P} hq={hq} hkv={hkv}", flush=True)
-    x = share_inputs(S, P, r, hq, hkv, d, "bf16", seed=cfg.seed)
     b = S // (2 * P)
+    print(f"[full-size] {cfg_name}: S={S} P={P} rank={r} hq={hq} hkv={hkv}", flush=True)
     if cfg.permute_heads:
-        # Q of the share = head group 0 of the permuted [2b][H][d] tensor
-        H = cfg.permute_heads
-        pre = synth.blocks_tensor(cfg.seed, synth.T_QPRE, synth.paired_blocks(P, r), b, H, d, "bf16")
-        src = torch.from_numpy(pre.view(np.int16)).cuda()
-        dst = torch.empty((H // hq, 2 * b, hq, d), dtype=torch.int16, device="cuda")
-        B.head_permute(src, dst, 2 * b, H, d, H // hq, 2, 0)
-        torch.cuda.synchronize()
-        x["q"] = dst[0].cpu().numpy().view(np.uint16)
-        assert np.array_equal(x["q"], oracle.head_permute(pre, H // hq)[0])
-        del src, dst
-    _, got = run_share(S, cfg.inner, cfg.outer, r, hq, hkv, d, "bf16", x)
+        H, Hkv, hp = cfg.permute_heads, hkv * (cfg.permute_heads // hq), cfg.permute_heads // hq
+        x = head_parallel_inputs(S, P, r, H, Hkv, d, hp, 0, seed=cfg.seed)
+        ring, got = run_head_parallel(S, cfg.inner, cfg.outer, r, H, Hkv, d, hp, 0, x)
+        ring = ring.ring
+    else:
+        x = share_inputs(S, P, r, hq, hkv, d, "bf16", seed=cfg.seed)
+        ring, got = run_share(S, cfg.inner, cfg.outer, r, hq, hkv, d, "bf16", x)
+    print("[full-size] GPU share done; oracle samples", flush=True)
     pos = oracle.zigzag_positions(S, P, r)
-    rows = _sample_rows(b, 16, cfg.seed)
+    rows = _sample_rows(b, 16, cfg.seed + r)
     heads = sorted({0, G - 1, hq // 2, hq - 1})
+    delta = ring.delta.cpu().numpy()
     for h in heads:
         g = h // G
         kg = widen(x["k_nat"][:, g:g + 1], "bf16")
@@ -218,21 +317,23 @@ def test_full_size_share_sampled(cfg_name):
         res = oracle.share_backward(qr, kg, vg, dor, pos[rows], scale, row_block=16)
         assert_close(f"O h{h}", got["O"][rows][:, h:h + 1], res["O"], "bf16")
         assert_close(f"LSE h{h}", got["LSE"][h:h + 1, rows], res["LSE"], "bf16", is_lse=True)
+        assert_close(f"D h{h}", delta[h:h + 1, rows], res["D"], "bf16")
         assert_close(f"dQ h{h}", got["dQ"][rows][:, h:h + 1], res["dQ"], "bf16")
-    # late keys: positions S-64 .. S-1 = chunk 0's back block tail
-    key_pos = np.arange(S - 64, S)
-    key_rows = b + (key_pos - (2 * P - 1) * b)          # rows of chunk 0 (and of this rank)
-    for g in sorted({0, hkv - 1}):
-        hs_ = slice(g * G, (g + 1) * G)
-        kg = widen(x["k_nat"][:, g:g + 1], "bf16")
-        vg = widen(x["v_nat"][:, g:g + 1], "bf16")
-        qr = widen(x["q"][key_rows][:, hs_], "bf16")
-        dor = widen(x["do"][key_rows][:, hs_], "bf16")
-        fw = oracle.share_backward(qr, kg, vg, dor, pos[key_rows], scale, row_block=16)
-        _, dk, dv = oracle.step_backward(qr, kg[key_pos], vg[key_pos], dor, fw["LSE"], fw["D"],
-                                         pos[key_rows], key_pos, scale)
-        assert_close(f"dK late g{g}", got["dK"][0][key_rows][:, g:g + 1], dk, "bf16")
-        assert_close(f"dV late g{g}", got["dV"][0][key_rows][:, g:g + 1], dv, "bf16")
+    # dK/dV of sampled keys: every local row of the group's heads contributes
+    lse_all = got["LSE"].astype(np.float64)
+    for j in sorted({0, 1, P - 1}):
+        kp_all = oracle.zigzag_positions(S, P, j)
+        keys = _sample_keys(b, cfg.seed + 31 * j)
+        for g in sorted({0, hkv - 1}):
+            hs_ = slice(g * G, (g + 1) * G)
+            kg = widen(x["k_nat"][kp_all[keys]][:, g:g + 1], "bf16")
+            vg = widen(x["v_nat"][kp_all[keys]][:, g:g + 1], "bf16")
+            _, dk, dv = oracle.step_backward(widen(x["q"][:, hs_], "bf16"), kg, vg,
+                                             widen(x["do"][:, hs_], "bf16"), lse_all[hs_],
+                                             delta[hs_].astype(np.float64), pos, kp_all[keys],
+                                             scale, row_block=2048)
+            assert_close(f"dK chunk {j} g{g}", got["dK"][j][keys][:, g:g + 1], dk, "bf16")
+            assert_close(f"dV chunk {j} g{g}", got["dV"][j][keys][:, g:g + 1], dv, "bf16")
     do64 = widen(x["do"], "bf16")
     for g in range(hkv):
         dv_sum = got["dV"][:, :, g].astype(np.float64).sum(axis=(0, 1))
@@ -240,3 +341,11 @@ def test_full_size_share_sampled(cfg_name):
         np.testing.assert_allclose(dv_sum, want_sum, atol=1e-3 * np.abs(want_sum).max() + 1e-2)
         dk_g = got["dK"][:, :, g].astype(np.float64)
         assert np.abs(dk_g.sum(axis=(0, 1))).max() <= 1e-3 * np.abs(dk_g).sum(axis=(0, 1)).max()
+    if cfg_name == "llama3_8b_cp8_128k":
+        q, do = to_device(x["q"], "bf16"), to_device(x["do"], "bf16")
+        K, V = to_device(x["k_ch"], "bf16"), to_device(x["v_ch"], "bf16")
+        dq2, dk2, dv2 = ring.backward(q, K, V, do)
+        torch.cuda.synchronize()
+        assert np.array_equal(dq2.cpu().numpy(), got["dQ"]), "dQ not bitwise repeatable"
+        assert np.array_equal(dk2.cpu().numpy(), got["dK"]), "dK not bitwise repeatable"
+        assert np.array_equal(dv2.cpu().numpy(), got["dV"]), "dV not bitwise repeatable"

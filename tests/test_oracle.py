@@ -121,6 +121,42 @@ def test_head_permute_brute_force_and_roundtrip():
         im.head_permute(x, 3)
 
 
+def _strided_head_permute(src, P):
+    """The other plausible grouping (destination p gets heads p, p+P, p+2P, ...),
+    kept here only as the negative case of the GQA-invariant pin below."""
+    S, H, d = src.shape
+    return np.stack([src[:, p::P, :] for p in range(P)])
+
+
+@pytest.mark.parametrize("H, Hkv, P", [(8, 4, 2), (8, 2, 2), (12, 4, 4), (32, 8, 4)])
+def test_head_permute_grouping_keeps_gqa_groups(H, Hkv, P):
+    """Pin of the head grouping by what the head-parallel split must preserve
+    ("Guide to LoongTrain", "The Scalability Limits of DeepSpeed Ulysses": every
+    head-parallel rank must receive whole KV heads, with their query heads).
+
+    Attention of the full-head tensors restricted to the query heads of group p
+    must equal attention of the p-th permuted Q/K/V run on its own (query head
+    h uses KV head h div (H/Hkv) before and after the permute). The strided
+    grouping, which passes the round trip and P = 1, must fail this."""
+    S, Pr, r, d = 64, 2, 1, 8
+    g = rng(H * 100 + Hkv * 10 + P)
+    pos = im.zigzag_positions(S, Pr, r)
+    q = g.standard_normal((len(pos), H, d))
+    k = g.standard_normal((S, Hkv, d))
+    v = g.standard_normal((S, Hkv, d))
+    full, _ = att.share_forward(q, k, v, pos, 0.3)
+    Hp = H // P
+    qp, kp, vp = im.head_permute(q, P), im.head_permute(k, P), im.head_permute(v, P)
+    for p in range(P):
+        o, _ = att.share_forward(qp[p], kp[p], vp[p], pos, 0.3)
+        np.testing.assert_allclose(o, full[:, p * Hp:(p + 1) * Hp], rtol=0, atol=1e-12)
+    if Hkv > 1 and H // Hkv > 1:
+        qs, ks, vs = (_strided_head_permute(x, P) for x in (q, k, v))
+        worst = max(np.abs(att.share_forward(qs[p], ks[p], vs[p], pos, 0.3)[0]
+                           - full[:, p::P]).max() for p in range(P))
+        assert worst > 1e-3
+
+
 # ----------------------------------------------------------------------------- forward
 
 def make_share(S, P, r, hq, hkv, d, seed):

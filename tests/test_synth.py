@@ -21,3 +21,12 @@ def test_block_draws_are_deterministic_and_independent():
     c = synth.blocks_tensor(7, synth.T_V, [4], 8, 2, 4, "f32")
     assert not np.array_equal(b, c)
     assert synth.paired_blocks(4, 1) == [1, 6]
+
+
+def test_head_subsets_draw_the_same_values():
+    """A head group drawn on its own equals the same heads of the full draw (the
+    head-parallel share's inputs exist without the other groups')."""
+    full = synth.blocks_tensor(11, synth.T_Q, [0, 5], 16, 8, 4, "bf16")
+    part = synth.blocks_tensor(11, synth.T_Q, [0, 5], 16, range(4, 6), 4, "bf16")
+    assert np.array_equal(full[:, 4:6], part)
+    assert full.dtype == np.uint16 and full.shape == (32, 8, 4)
