@@ -380,62 +380,46 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     }
 }
 
-// dK/dV kernel tuning: LDS reads issued ahead of the score products, and the
-// wave priority of the P waves (whose chain sets the step time)
-#ifndef RA_DKV_AHEAD
-#define RA_DKV_AHEAD 8
-#endif
-#ifndef RA_DKV_PPRIO
-#define RA_DKV_PPRIO 1
-#endif
-
-// (2) dK, dV, key-stationary: a workgroup of 8 waves (two per SIMD) owns 128
-//     keys of one KV head and walks the 64-row query tiles of every query head
-//     of the group. The waves come in pairs on the same 32 keys: the P wave
-//     computes S = Q K^T (K held as the MFMA B operand), P = exp(S - LSE) and
-//     dV^T += dO^T P, and hands P (bf16) to its partner through LDS; the
-//     partner (V held) computes dP = dO V^T of the same tile in the same step
-//     and, one step later, dS = P (dP - D) and dK^T += Q^T dS. Each wave keeps
-//     one accumulator set (the dK wave also one tile of dP), so both roles fit
-//     two waves per SIMD, and no product is computed twice. The dK wave
-//     starts each step with the dS products of the previous tile, the P wave
-//     with its score products, so their VALU-heavy phases do not coincide.
-//     Q tiles reach LDS by DMA two steps ahead (four rotating buffers), dO
-//     tiles one step ahead (two buffers), both XOR-swizzled, with the tile's
-//     LSE (log2 units) and D; one barrier per step. Query rows are fed in
-//     sigma order, so P and dS are directly B operands of the dV / dK
-//     products, whose A operands are read transposed from the same tiles.
-//     Each dK/dV element has one writer.
+// (2) dK, dV, key-stationary, symmetric wave pairs: a workgroup of 8 waves
+//      (two per SIMD) owns 128 keys of one KV head and walks the 64-row query
+//      tiles of every query head of the group. Waves w and w ^ 4 share 32 keys;
+//      wave half hf = w / 4 computes, for tile rows 32 hf .. 32 hf + 31,
+//      S = Q K^T and dP = dO V^T (K and V of its key held as MFMA B operands),
+//      then P = exp(S - LSE) and dS = P (dP - D) in fp32, each rounded once to
+//      bf16, and hands them to its partner through LDS. After a barrier each
+//      wave accumulates dV^T += dO^T P and dK^T += Q^T dS over all 64 rows for
+//      the d columns 64 hf / (D/128) .. of its half, its own rows' P/dS from
+//      registers and its partner's from LDS. Q and dO tiles reach LDS by DMA
+//      one step ahead (two buffers each, XOR-swizzled), with the tile's LSE
+//      (log2 units) and D. Every dK/dV element has one writer.
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
   constexpr int NW = 8;
-  constexpr int KB = 128;  // keys per workgroup
-  constexpr int QT = 64;   // query rows per tile
-  constexpr int NC = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int TB = QT * D;  // elements per Q / dO tile
-  constexpr int PB = QT * 32;  // elements of P per key group
+  constexpr int KB = 128;      // keys per workgroup
+  constexpr int QT = 64;       // query rows per tile
+  constexpr int NC = D / 16;   // 16-wide d chunks (contraction steps of S and dP)
+  constexpr int NDH = D / 64;  // 32-wide d blocks in a wave's half of d
+  constexpr int TB = QT * D;   // elements per Q / dO tile
+  constexpr int XB = 4 * 64 * 8;  // exchange elements per wave: 4 chunks x 64 lanes x 8
   __shared__ __attribute__((aligned(1024))) bf16_t sQ0[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sQ1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sQ2[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sQ3[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sG0[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sG1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sP[2 * 4 * PB];  // two slots
+  __shared__ __attribute__((aligned(1024))) bf16_t sX[NW * XB];  // P and dS hand-off
   __shared__ __attribute__((aligned(16))) float sL[2][QT];  // LSE * log2(e) (+inf: no contribution)
-  __shared__ __attribute__((aligned(16))) float sD[4][QT];
+  __shared__ __attribute__((aligned(16))) float sD[2][QT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const bool pwave = wave < 4;  // role: P / dV (else dS / dK)
-  const int kw = wave & 3;      // key group of the wave pair
+  const int kw = wave & 3;     // key group of the pair
+  const int hf = wave >> 2;    // row half (S, dP, P, dS) and d half (dK, dV)
   const int l32 = lane & 31, hi = lane >> 5;
   const int srow = sigma32(l32);
 
   const int logical = xcd_remap(blockIdx.x, p.hkv * n_kt, p.hkv);
   const int g = logical / n_kt;
-  const int kt = logical % n_kt;  // earlier keys (seen by more queries) first
+  const int kt = logical % n_kt;
   const int64_t lq = p.qm.len, lk = p.km.len;
   const int64_t key0 = (int64_t)kt * KB;
   const int64_t key1 = key0 + KB < lk ? key0 + KB : lk;
@@ -443,314 +427,227 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   const int64_t mykey = wkey0 + l32;
   const bool key_ok = mykey < lk;
   const int kpos = key_ok ? (int)seg_pos(p.km, mykey) : INT_MAX;
-  int64_t gk_lo, gk_hi, wk_lo = 0, wk_hi = 0;
+  int64_t gk_lo, gk_hi;
   seg_bounds(p.km, key0, key1, gk_lo, gk_hi);
   const bool wave_has_keys = wkey0 < lk;
-  if (wave_has_keys) seg_bounds(p.km, wkey0, wkey0 + 32 < lk ? wkey0 + 32 : lk, wk_lo, wk_hi);
 
-  // K (P wave) or V (dK wave) of this lane's key as the B operand: d = 16c + 8*hi .. +8
-  bf16x8 breg[NC];
+  // K and V of this lane's key as B operands: d = 16c + 8*hi .. +8
+  bf16x8 kreg[NC], vreg[NC];
   {
-    const bf16_t* Bp = pwave ? (const bf16_t*)p.k + (int64_t)g * p.k_hs + mykey * p.k_ss
-                             : (const bf16_t*)p.v + (int64_t)g * p.v_hs + mykey * p.v_ss;
+    const bf16_t* Kp = (const bf16_t*)p.k + (int64_t)g * p.k_hs + mykey * p.k_ss + 8 * hi;
+    const bf16_t* Vp = (const bf16_t*)p.v + (int64_t)g * p.v_hs + mykey * p.v_ss + 8 * hi;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 z = {};
-      breg[c] = key_ok ? *(const bf16x8*)(Bp + 8 * hi + 16 * c) : z;
+      kreg[c] = key_ok ? *(const bf16x8*)(Kp + 16 * c) : z;
+      vreg[c] = key_ok ? *(const bf16x8*)(Vp + 16 * c) : z;
     }
   }
-  f32x16 acc[ND];  // dV^T (P wave) or dK^T (dK wave): lane = key, registers = d
+  // dV^T, dK^T of this lane's key: register r of block db is d row
+  // (D/2) hf + 32 db + 8 (r/4) + 4 hi + r%4
+  f32x16 dvacc[NDH], dkacc[NDH];
 #pragma unroll
-  for (int db = 0; db < ND; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < NDH; ++db) {
+    dvacc[db] = f32x16{};
+    dkacc[db] = f32x16{};
+  }
 
-  // iterations: (query tile t, query head of the group hh) pairs, tiles in
-  // descending order with the heads innermost, so the workgroups of one KV
-  // head read the same Q / dO tiles at about the same time until each reaches
-  // its first visible tile (the visible tiles are suffixes, different for each
-  // key block on the diagonal step; a shared order keeps them in L2);
-  // hh == group marks the end
+  // (query tile, query head) iterations: tiles in descending order with the
+  // group's heads innermost (the workgroups of a KV head then read the same
+  // Q / dO tiles at about the same time); hh == group marks the end
   const QueryTiles<QT> qt_wg(p.qm, p.causal, gk_lo, gk_hi);
-  const QueryTiles<QT> qt_w(p.qm, p.causal, wk_lo, wk_hi);
-  const int t_last = qt_wg.prev(qt_wg.n - 1);
-  // the visible (tile, head) after (t, hh), or (-1, group)
   auto advance = [&](int& hh, int& t) {
     if (++hh < p.group) return;
     t = qt_wg.prev(t - 1);
     hh = t >= 0 ? 0 : p.group;
   };
 
-  DmaSwz<QT, D, NW, 2> qst, gst;
+  DmaSwz<QT, D, NW, 3> qst, gst;
   qst.init(p.q_ss, wave, lane);
   gst.init(p.do_ss, wave, lane);
-  // buffers by step position (compile-time, so DMA into one buffer never
-  // orders reads of another)
-  auto qbuf = [&](auto b) -> bf16_t* {
-    constexpr int B = decltype(b)::value & 3;
-    return B == 0 ? sQ0 : (B == 1 ? sQ1 : (B == 2 ? sQ2 : sQ3));
-  };
-  auto gbuf = [&](auto b) -> bf16_t* {
-    constexpr int B = decltype(b)::value & 1;
-    return B == 0 ? sG0 : sG1;
-  };
-  // (an invalid tile is still issued, with no rows in range, so that every
-  // step issues the same number of loads; it fills a free buffer with zeros)
-  auto stage_q = [&](int hh, int t, auto b, bool valid) {
-    const int h = g * p.group + (valid ? hh : 0);
-    const int64_t q0 = valid ? (int64_t)t * QT : 0;
-    qst.issue_untracked((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, q0, valid ? lq : q0,
-                        qbuf(b));
-  };
-  auto stage_g = [&](int hh, int t, auto b) {
+  auto stage = [&](int hh, int t, auto b) {
+    constexpr int B = decltype(b)::value;
     const int h = g * p.group + hh;
-    gst.issue_untracked((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, (int64_t)t * QT, lq,
-                        gbuf(b));
+    qst.issue((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, (int64_t)t * QT, lq, B ? sQ1 : sQ0);
+    gst.issue((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, (int64_t)t * QT, lq,
+              B ? sG1 : sG0);
   };
-  // LSE and D of a tile: wave 0 loads them into registers two steps before the
-  // tile is used and writes them to LDS at the end of the next step, so the
-  // loads never stall a step
-  float pl = -INFINITY, pd = 0.f;  // loaded one step ago
-  float nl = -INFINITY, nd = 0.f;  // loaded in this step
-  auto load_ld = [&](int hh, int t, float& l, float& d) {
+  // LSE and D of a tile: wave 0 loads them into registers one step before
+  // they are written to LDS (at the start of the step before their tile's), so
+  // the global loads never stall a step
+  float pl = -INFINITY, pd = 0.f;
+  auto load_ld = [&](int hh, int t) {
     if (wave == 0) {
       const int h = g * p.group + hh;
       const int64_t row = (int64_t)t * QT + lane;
-      l = -INFINITY;
-      d = 0.f;
+      pl = -INFINITY;
+      pd = 0.f;
       if (row < lq) {
-        l = p.lse_in[(int64_t)h * lq + row];
-        d = p.delta[(int64_t)h * lq + row];
+        pl = p.lse_in[(int64_t)h * lq + row];
+        pd = p.delta[(int64_t)h * lq + row];
       }
     }
   };
-  auto store_ld = [&](auto b, float l, float d) {
+  auto store_ld = [&](auto b) {
     constexpr int B = decltype(b)::value;
     if (wave == 0) {
-      sL[B & 1][lane] = l == -INFINITY ? INFINITY : l * kLog2e;  // empty row: no contribution
-      sD[B & 3][lane] = d;
+      sL[B][lane] = pl == -INFINITY ? INFINITY : pl * kLog2e;  // empty row: no contribution
+      sD[B][lane] = pd;
     }
   };
 
   // per-lane byte offsets in a swizzled tile: 16-byte row reads of chunk
-  // 2*c + hi of row qb*32 + sigma(l32), and transposing reads of rows
-  // 16*cq + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3).
-  // The swizzle is an XOR on the chunk index, so the offset for chunk c
-  // (block db) is that of chunk 0 (block 0) XOR 32*c (64*db); the bases are
-  // passed through an opaque copy every step, so the derived offsets are
-  // formed where they are used instead of being held across the loop.
+  // 2c + hi of row 32 hf + sigma(l32) (XOR 32 c), and transposing reads of
+  // rows 16 cq + 8 hi + gi/4 (+4) at d = 32 db + 16 (grp & 1) + 4 (gi & 3)
+  // (XOR 64 db)
   const int grp = lane >> 4, gi = lane & 15;
-  const int roff_base = swz_off<D>(srow, hi);
-  const int toff_base0 = swz_off<D>(8 * hi + (gi >> 2), 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
-  const int toff_base1 = swz_off<D>(8 * hi + (gi >> 2) + 4, 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
-  int roff0 = roff_base, toff0 = toff_base0, toff1 = toff_base1;
-  auto refresh_offsets = [&]() {
-    roff0 = roff_base;
-    toff0 = toff_base0;
-    toff1 = toff_base1;
-    asm volatile("" : "+v"(roff0), "+v"(toff0), "+v"(toff1));
-  };
-  // P hand-off slot of this lane: block (qb, hf) of key group kw, 16 bytes per lane
-  const int p_lane = kw * PB + lane * 8;
+  const int roff = 32 * hf * 2 * D + swz_off<D>(srow, hi);
+  const int toff0 = swz_off<D>(8 * hi + (gi >> 2), 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  const int toff1 = swz_off<D>(8 * hi + (gi >> 2) + 4, 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  // hand-off slots: chunk cq (16 rows) of wave w at sX[w][cq][lane][8]
+  bf16_t* const x_mine = sX + wave * XB + lane * 8;
+  const bf16_t* const x_partner = sX + (wave ^ 4) * XB + lane * 8;
 
-  // A x (B operand) over the tile's two 32-row query blocks: register r of
-  // block qb is query row qb*32 + 16*(r/8) + 8*hi + r%8, the lane's key
-  auto row_products = [&](const char* tile, f32x16 (&x)[2]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      x[qb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        x[qb] = mfma32(*(const bf16x8*)(tile + qb * 32 * 2 * D + (roff0 ^ (32 * c))), breg[c], x[qb]);
-    }
-  };
-  // acc^T += tile^T B' over 16 query rows cq (B' = P or dS chunk in bf16)
-  auto col_products = [&](const char* tile, int cq, const bf16x8& bv) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const char* a = tile + 16 * cq * 2 * D;
-      const bf16x8 av = __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + (toff0 ^ (64 * db)))),
-                                                ds_read_tr((const bf16_t*)(a + (toff1 ^ (64 * db)))), 0,
-                                                1, 2, 3, 4, 5, 6, 7);
-      acc[db] = mfma32(av, bv, acc[db]);
-    }
-  };
+  f32x16 sacc, pacc;
+  bf16x8 pk[2], dsk[2];  // this wave's rows: chunks 2 hf + cc
 
-  // score block: S = Q K^T of the tile in buffer b into sc, with the tile
-  // reads issued AH products ahead
-  f32x16 sc[2];
-  auto scores = [&](auto b) {
-    row_products((const char*)qbuf(b), sc);
-    constexpr int AH = RA_DKV_AHEAD < 2 * NC ? RA_DKV_AHEAD : 2 * NC;
-    if (AH > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // LDS reads
+  // phase 1 of a step: S, dP of this wave's rows; P, dS; hand-off
+  auto phase1 = [&](int t, auto b) {
+    constexpr int B = decltype(b)::value;
+    const char* cQ = (const char*)(B ? sQ1 : sQ0);
+    const char* cG = (const char*)(B ? sG1 : sG0);
+    sacc = f32x16{};
+    pacc = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 2 * NC - AH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+    for (int c = 0; c < NC; ++c) {
+      sacc = mfma32(*(const bf16x8*)(cQ + (roff ^ (32 * c))), kreg[c], sacc);
+      pacc = mfma32(*(const bf16x8*)(cG + (roff ^ (32 * c))), vreg[c], pacc);
     }
-  };
-  // P wave at step position I (tile i): S, mask, P -> LDS slot I % 2,
-  // dV^T += dO^T P
-  auto p_step = [&](int t, auto pos) {
-    constexpr int I = decltype(pos)::value;
-    const char* cG = (const char*)gbuf(std::integral_constant<int, I>{});
-    scores(std::integral_constant<int, I>{});
-    // masking of the diagonal / ragged tiles: a uniform branch around
-    // branch-free selects that rewrite the scores in place (a whole second copy
-    // of the step would keep the accumulators in other registers and copy them
-    // back at the join)
-    if (!qt_w.mask_free(t)) {
+    // register r is row 32 hf + 16 (r/8) + 8 hi + r%8 of the tile, the lane's key
+    if (!qt_wg.mask_free(t)) {  // workgroup-uniform: one branch around branch-free selects
       const TileRows tq(p.qm, (int64_t)t * QT, QT);
-      const QMaskBounds mb(tq, kpos, key_ok, 8 * hi, p.causal);
+      const QMaskBounds mb(tq, kpos, key_ok, 32 * hf + 8 * hi, p.causal);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool vis = mb.row_visible(qb * 32 + 16 * (r >> 3) + (r & 7));
-          sc[qb][r] = vis ? sc[qb][r] : -INFINITY;
-        }
-    }
-    bf16_t* sp = sP + (I & 1) * 4 * PB + p_lane;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int qo = qb * 32 + 16 * hf + 8 * hi;
-        const f32x4 la = *(const f32x4*)(&sL[I & 1][qo]), lb = *(const f32x4*)(&sL[I & 1][qo + 4]);
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float l2 = e < 4 ? la[e] : lb[e - 4];
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[qb][8 * hf + e], p.scale_log2, -l2));
-        }
-        const bf16x8 pk = pack_bf16x8(pv);
-        *(bf16x8*)(sp + (2 * qb + hf) * 512) = pk;
-        col_products(cG, 2 * qb + hf, pk);
+      for (int r = 0; r < 16; ++r) {
+        const bool vis = mb.row_visible(16 * (r >> 3) + (r & 7));
+        sacc[r] = vis ? sacc[r] : -INFINITY;
       }
-  };
-  // dK wave at step position I: dS of tile i - 1 (its dP in dp, its P in
-  // slot (I - 1) % 2), dK^T += Q^T dS, then dP of tile i into dp
-  // (unconditionally: past the last tile it is discarded). The dS products
-  // come first, so the pair's VALU-heavy phases (softmax here, dS there) fall
-  // against the other wave's matrix products.
-  f32x16 dp[2];
-  auto k_step = [&](auto pos, auto ds_tag) {
-    constexpr int I = decltype(pos)::value;
-    constexpr bool DS = decltype(ds_tag)::value;
-    if (DS) {
-      const char* cQ = (const char*)qbuf(std::integral_constant<int, I + 3>{});
-      const bf16_t* sp = sP + ((I + 1) & 1) * 4 * PB + p_lane;
-      constexpr int DSL = (I + 3) & 3;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int qo = qb * 32 + 16 * hf + 8 * hi;
-          const f32x4 da = *(const f32x4*)(&sD[DSL][qo]), db_ = *(const f32x4*)(&sD[DSL][qo + 4]);
-          const bf16x8 pk = *(const bf16x8*)(sp + (2 * qb + hf) * 512);
-          float sv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float dl = e < 4 ? da[e] : db_[e - 4];
-            sv[e] = (float)pk[e] * (dp[qb][8 * hf + e] - dl);
-          }
-          col_products(cQ, 2 * qb + hf, pack_bf16x8(sv));
-        }
     }
-    row_products((const char*)gbuf(std::integral_constant<int, I>{}), dp);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int qo = 32 * hf + 16 * cc + 8 * hi;
+      const f32x4 la = *(const f32x4*)(&sL[B][qo]), lb = *(const f32x4*)(&sL[B][qo + 4]);
+      const f32x4 da = *(const f32x4*)(&sD[B][qo]), db_ = *(const f32x4*)(&sD[B][qo + 4]);
+      float pv[8], sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float l2 = e < 4 ? la[e] : lb[e - 4];
+        const float dl = e < 4 ? da[e] : db_[e - 4];
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * cc + e], p.scale_log2, -l2));
+        sv[e] = pv[e] * (pacc[8 * cc + e] - dl);
+      }
+      pk[cc] = pack_bf16x8(pv);
+      dsk[cc] = pack_bf16x8(sv);
+      *(bf16x8*)(x_mine + (2 * cc) * 512) = pk[cc];
+      *(bf16x8*)(x_mine + (2 * cc + 1) * 512) = dsk[cc];
+    }
+  };
+  // phase 2: dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows, for
+  // this wave's d half; chunk cq of rows is this wave's (registers) when
+  // cq / 2 == hf, else its partner's (LDS)
+  auto phase2 = [&](auto b) {
+    constexpr int B = decltype(b)::value;
+    // rows 32 hf' .. of the tile, hf' = the half of the chunk's owner
+    const char* cQ = (const char*)(B ? sQ1 : sQ0);
+    const char* cG = (const char*)(B ? sG1 : sG0);
+    const int own_row = 32 * hf * 2 * D, partner_row = 32 * (hf ^ 1) * 2 * D;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int cc = k & 1;
+      const bool own = k < 2;  // this wave's chunks first: no LDS read for their B operand
+      const bf16x8 pb = own ? pk[cc] : *(const bf16x8*)(x_partner + (2 * cc) * 512);
+      const bf16x8 sb = own ? dsk[cc] : *(const bf16x8*)(x_partner + (2 * cc + 1) * 512);
+      const int rowb = (own ? own_row : partner_row) + 16 * cc * 2 * D;
+#pragma unroll
+      for (int db = 0; db < NDH; ++db) {
+        const int dblk = 64 * (NDH * hf + db);  // byte XOR of the 32-wide d block
+        const char* ag = cG + rowb;
+        const char* aq = cQ + rowb;
+        const bf16x8 av = __builtin_shufflevector(ds_read_tr((const bf16_t*)(ag + (toff0 ^ dblk))),
+                                                  ds_read_tr((const bf16_t*)(ag + (toff1 ^ dblk))),
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+        dvacc[db] = mfma32(av, pb, dvacc[db]);
+        const bf16x8 aq8 = __builtin_shufflevector(ds_read_tr((const bf16_t*)(aq + (toff0 ^ dblk))),
+                                                   ds_read_tr((const bf16_t*)(aq + (toff1 ^ dblk))),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+        dkacc[db] = mfma32(aq8, sb, dkacc[db]);
+      }
+    }
   };
 
-  // Step i (position I = i % 4): Q and dO of tile i have landed at this
-  // step's barrier (Q of tile i + 1 may still be in flight); the DMA of dO of
-  // tile i + 1 goes to the dO buffer read by both roles one step ago, then
-  // that of Q of tile i + 2 to the Q buffer last read by the dK waves one step
-  // ago. The two roles run
-  // separate loops with the same barrier sequence, so each role's registers
-  // are allocated on their own.
-  int ch = t_last >= 0 ? 0 : p.group, ct = t_last;  // tile i
-  int nh = ch, nt = ct;                                    // tile i + 1
-  if (ch < p.group) advance(nh, nt);
-  bool have_prev = false;
-  // The Q DMA of the previous step is the last vector-memory operation issued
-  // and is read no earlier than the next step: the waits leave it in flight.
-  constexpr int QDMA = DmaSwz<QT, D, NW, 2>::PER;  // DMA instructions per lane per tile
-  static_assert((QT * 2 * D / 1024) % NW == 0, "every wave issues QDMA loads per tile");
-  auto step = [&](auto pos, auto role) {
-    constexpr int I = decltype(pos)::value;
-    constexpr bool PW = decltype(role)::value;
-    wait_vmem_n<QDMA>();
-    barrier_lds();  // Q(i), dO(i), LSE(i), D(i-1), P(i-1) visible; DMA targets free
-    refresh_offsets();
-    const bool cur = ch < p.group;
-    const bool nxt = nh < p.group;
-    int n2h = nh, n2t = nt;
-    if (nxt) advance(n2h, n2t);
-    if (nxt) stage_g(nh, nt, std::integral_constant<int, I + 1>{});
-    if (n2h < p.group) load_ld(n2h, n2t, nl, nd);
-    asm volatile("" ::: "memory");  // keep the Q DMA last
-    stage_q(n2h, n2t, std::integral_constant<int, I + 2>{}, n2h < p.group);
-    if (wave_has_keys) {
-      if (PW) {
-        if (cur) p_step(ct, pos);
-      } else {
-        if (have_prev)
-          k_step(pos, std::true_type{});
-        else
-          k_step(pos, std::false_type{});
-      }
+  // Step i: tile i is in buffer i % 2 (landed at this step's first barrier);
+  // the DMA of tile i + 1 goes to the other buffer (last read in the previous
+  // step's phase 2, before this barrier).
+  int ch = qt_wg.prev(qt_wg.n - 1) >= 0 ? 0 : p.group, ct = qt_wg.prev(qt_wg.n - 1);
+  auto step = [&](auto b) {
+    constexpr int B = decltype(b)::value;
+    using NB = std::integral_constant<int, B ^ 1>;
+    wait_vmem();
+    __syncthreads();  // tile i, LSE/D of tile i visible; the other buffers free
+    int nh = ch, nt = ct;
+    advance(nh, nt);
+    if (nh < p.group) {
+      store_ld(NB{});  // tile i + 1's, loaded one step ago
+      stage(nh, nt, NB{});
+      int n2h = nh, n2t = nt;
+      advance(n2h, n2t);
+      if (n2h < p.group) load_ld(n2h, n2t);
     }
-    if (nxt) store_ld(std::integral_constant<int, I + 1>{}, pl, pd);  // visible at the next barrier
-    pl = nl;
-    pd = nd;
-    have_prev = cur;
+    if (wave_has_keys) phase1(ct, b);
+    barrier_lds();  // the hand-off is visible
+    if (wave_has_keys) phase2(b);
     ch = nh;
     ct = nt;
-    nh = n2h;
-    nt = n2t;
-    return have_prev;
+    return ch < p.group;
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
-  using P3 = std::integral_constant<int, 3>;
   if (ch < p.group) {
-    stage_q(ch, ct, P0{}, true);
-    stage_q(nh, nt, P1{}, nh < p.group);
-    stage_g(ch, ct, P0{});
-    load_ld(ch, ct, pl, pd);
-    store_ld(P0{}, pl, pd);
-    if (nh < p.group) load_ld(nh, nt, pl, pd);
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    stage(ch, ct, B0{});
+    load_ld(ch, ct);
     wait_vmem();
-    __syncthreads();
-    // four-step unroll: buffer indices are compile-time constants
-    if (pwave) {
-      const std::true_type r{};
-      if (RA_DKV_PPRIO) __builtin_amdgcn_s_setprio(RA_DKV_PPRIO);
-      while (step(P0{}, r) && step(P1{}, r) && step(P2{}, r) && step(P3{}, r)) {
-      }
-    } else {
-      const std::false_type r{};
-      while (step(P0{}, r) && step(P1{}, r) && step(P2{}, r) && step(P3{}, r)) {
-      }
+    store_ld(B0{});
+    {
+      int nh = ch, nt = ct;
+      advance(nh, nt);
+      if (nh < p.group) load_ld(nh, nt);
     }
-    wait_vmem();  // the last (empty) Q DMA lands before the workgroup's LDS is released
+    // buffers alternate; unrolled so each buffer is a distinct array
+    while (step(B0{}) && step(B1{})) {
+    }
   }
 
-  // ---- epilogue: lanes = keys, registers = d rows 8*(r/4) + 4*hi + r%4
+  // ---- epilogue: lanes = keys, registers = d rows
   if (!key_ok) return;
-  float* dst = (pwave ? p.dv : p.dk) + mykey * p.dk_ss + (int64_t)g * p.dk_hs;
-  const float out_scale = pwave ? 1.f : p.scale;
+  const int64_t obase = mykey * p.dk_ss + (int64_t)g * p.dk_hs + (D / 2) * hf;
 #pragma unroll
-  for (int db = 0; db < ND; ++db)
+  for (int db = 0; db < NDH; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f32x4 a;
+      f32x4 a, c;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = acc[db][4 * i + j] * out_scale;
-      f32x4* pa = (f32x4*)(dst + 32 * db + 8 * i + 4 * hi);
-      if (p.dkv_accumulate) a += *pa;
-      *pa = a;
+      for (int j = 0; j < 4; ++j) {
+        a[j] = dvacc[db][4 * i + j];
+        c[j] = dkacc[db][4 * i + j] * p.scale;
+      }
+      f32x4* pv = (f32x4*)(p.dv + obase + 32 * db + 8 * i + 4 * hi);
+      f32x4* pk4 = (f32x4*)(p.dk + obase + 32 * db + 8 * i + 4 * hi);
+      if (p.dkv_accumulate) {
+        a += *pv;
+        c += *pk4;
+      }
+      *pv = a;
+      *pk4 = c;
     }
 }
 

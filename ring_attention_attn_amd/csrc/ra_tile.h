@@ -60,145 +60,25 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Transpose a 4-row x 8-column bf16 block held as four 8-wide rows into eight
-// 4-wide columns (column e = {row0[e], row1[e], row2[e], row3[e]}).
-__device__ __forceinline__ void transpose4x8(const bf16x8 (&in)[4], bf16x4 (&out)[8]) {
-  typedef __attribute__((__vector_size__(16 * sizeof(__bf16)))) __bf16 bf16x16;
-  const bf16x16 p01 = __builtin_shufflevector(in[0], in[1], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5,
-                                              13, 6, 14, 7, 15);
-  const bf16x16 p23 = __builtin_shufflevector(in[2], in[3], 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5,
-                                              13, 6, 14, 7, 15);
-  out[0] = __builtin_shufflevector(p01, p23, 0, 1, 16, 17);
-  out[1] = __builtin_shufflevector(p01, p23, 2, 3, 18, 19);
-  out[2] = __builtin_shufflevector(p01, p23, 4, 5, 20, 21);
-  out[3] = __builtin_shufflevector(p01, p23, 6, 7, 22, 23);
-  out[4] = __builtin_shufflevector(p01, p23, 8, 9, 24, 25);
-  out[5] = __builtin_shufflevector(p01, p23, 10, 11, 26, 27);
-  out[6] = __builtin_shufflevector(p01, p23, 12, 13, 28, 29);
-  out[7] = __builtin_shufflevector(p01, p23, 14, 15, 30, 31);
-}
-
-// ---- global -> register staging through buffer loads. A buffer descriptor
-// spans the rows [row0, nrows) of one head (row stride ss elements); reads past
-// its end return zeros, so ragged tails need no selects. The descriptor is
-// built per tile from uniform values (scalar arithmetic), and each thread's
-// byte offsets inside a tile are fixed, so a load costs no vector ALU work.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16_t* base, int64_t ss,
-                                                            int64_t row0, int64_t nrows) {
-  int64_t bytes = (nrows - row0) * ss * 2;
-  bytes = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * ss), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-
-// Row-major staging of a T x D bf16 tile into lds[row * STR + col]: 16-byte
-// chunk c (stride 256 over the workgroup) is row c / (D/8), column
-// 8*(c % (D/8)), so every wave writes whole rows (conflict-free stores).
-template <int T, int D, int STR>
-struct RowStage {
-  static constexpr int CPR = D / 8;
-  static constexpr int N = T * CPR / 256;
-  static_assert(N >= 1 && T * CPR % 256 == 0, "tile must be a multiple of 256 chunks");
-  uint32_t voff[N];
-  int lds0;
-  bf16x8 v[N];
-  __device__ __forceinline__ void init(int64_t ss, int tid) {
-    const int row = tid / CPR, col = 8 * (tid % CPR);
-    lds0 = row * STR + col;
-#pragma unroll
-    for (int i = 0; i < N; ++i) voff[i] = (uint32_t)(((row + i * (256 / CPR)) * ss + col) * 2);
-  }
-  __device__ __forceinline__ void load(const bf16_t* base, int64_t ss, int64_t row0,
-                                       int64_t nrows) {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = buf_load16(r, voff[i]);
-  }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) *(bf16x8*)(lds + lds0 + i * (256 / CPR) * STR) = v[i];
-  }
-};
-
-// Transposed staging of a T x D bf16 tile into lds[col * STR + row]: thread
-// c < (T/4)*(D/8) loads rows 4*(c % (T/4)) .. +3 at columns 8*(c / (T/4)) .. +8
-// and writes eight 4-row columns (64-bit stores) after a register transpose.
-template <int T, int D, int STR>
-struct ColStage {
-  static constexpr int RG = T / 4;
-  static constexpr int NTH = RG * (D / 8);
-  static_assert(NTH <= 256 && NTH % 64 == 0, "one pass of whole waves");
-  uint32_t voff0, vstep;
-  int lds0;
-  bool active;
-  bf16x8 v[4];
-  __device__ __forceinline__ void init(int64_t ss, int tid) {
-    active = tid < NTH;
-    const int rg = tid % RG, col = 8 * (tid / RG);
-    voff0 = (uint32_t)((4 * rg * ss + col) * 2);
-    vstep = (uint32_t)(ss * 2);
-    lds0 = col * STR + 4 * rg;
-  }
-  __device__ __forceinline__ void load(const bf16_t* base, int64_t ss, int64_t row0,
-                                       int64_t nrows) {
-    if (!active) return;
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = buf_load16(r, voff0 + j * vstep);
-  }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-    if (!active) return;
-    bf16x4 t[8];
-    transpose4x8(v, t);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) *(bf16x4*)(lds + lds0 + e * STR) = t[e];
-  }
-};
-
 // ---- global -> LDS staging by LDS-DMA buffer loads (no registers, no ds_write).
-// The tile's T rows of D bf16 are laid out in LDS with a row stride of RSB
-// bytes (padding chosen per use for conflict-free reads). Instruction j of the
-// workgroup fills LDS bytes [1024 j, 1024 j + 1024): lane i writes the 16 bytes
-// at p = 1024 j + 16 i, i.e. chunk (p % RSB) / 16 of tile row p / RSB; a lane
-// that lands in a row's padding loads that row's first chunk (harmless). Rows
-// past the descriptor's range read as zero.
+// A buffer descriptor spans the rows [row0, row0 + rows) of one head (row
+// stride ss elements); reads past its end return zeros, so ragged tails need no
+// selects. Instruction j of the workgroup fills LDS bytes [1024 j, 1024 j +
+// 1024): lane i writes the 16 bytes at 1024 j + 16 i.
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int T, int D, int RSB, int NW>
-struct DmaStage {
-  static constexpr int NJ = T * RSB / 1024;
-  static constexpr int PER = (NJ + NW - 1) / NW;
-  static_assert(T * RSB % 1024 == 0 && RSB % 16 == 0 && RSB >= 2 * D, "whole 1 KiB blocks");
-  uint32_t voff[PER];
-  int wave;
-  __device__ __forceinline__ void init(int64_t ss, int wave_, int lane) {
-    wave = wave_;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int p = 1024 * (wave + k * NW) + 16 * lane;
-      const int row = p / RSB;
-      int ch = (p % RSB) / 16;
-      ch = ch < D / 8 ? ch : 0;
-      voff[k] = (uint32_t)(((int64_t)(row < T ? row : 0) * ss + 8 * ch) * 2);
-    }
-  }
-  // tile rows [row0, row0 + T) of `base` (row stride ss elements) into `lds`
-  __device__ __forceinline__ void issue(const bf16_t* base, int64_t ss, int64_t row0,
-                                        int64_t nrows, bf16_t* lds) const {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int j = wave + k * NW;
-      if (j < NJ)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((char*)lds + 1024 * j), 16,
-                                                 voff[k], 0, 0, 0);
-    }
-  }
-};
+// Descriptor of the T-row tile starting at row0 of a tensor with nrows rows:
+// only rows that exist are in range. row_bytes = ss * 2; T * row_bytes < 2^31
+// (the host rejects larger strides), so the range is 32-bit arithmetic.
+template <int T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16_t* base, int64_t ss,
+                                                            uint32_t row_bytes, int64_t row0,
+                                                            int64_t nrows) {
+  const int64_t left = nrows - row0;
+  const int rows = left <= 0 ? 0 : (left >= T ? T : (int)left);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * ss), (short)0,
+                                           (int)(rows * row_bytes), 0x00020000);
+}
 
 // ---- XOR-swizzled row-major tiles (no padding): rows of D bf16, 16-byte
 // chunk c of row r stored at chunk c ^ swz(r). Reads of one chunk from 16
@@ -228,9 +108,11 @@ struct DmaSwz {
   static constexpr int PER = (NJ + NW - 1) / NW;
   static_assert(T * 2 * D % 1024 == 0, "whole 1 KiB blocks");
   uint32_t voff[PER];
+  uint32_t row_bytes;
   int wave;
   __device__ __forceinline__ void init(int64_t ss, int wave_, int lane) {
     wave = wave_;
+    row_bytes = (uint32_t)(ss * 2);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int pb = 1024 * (wave + k * NW) + 16 * lane;
@@ -241,13 +123,14 @@ struct DmaSwz {
       voff[k] = (uint32_t)(((int64_t)row * ss + 8 * c) * 2);
     }
   }
+  // tile rows [row0, row0 + T) of `base` (row stride ss elements) into `lds`
   __device__ __forceinline__ void issue(const bf16_t* base, int64_t ss, int64_t row0,
                                         int64_t nrows, bf16_t* lds) const {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<T>(base, ss, row_bytes, row0, nrows);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = wave + k * NW;
-      if (j < NJ)
+      if (NJ % NW == 0 || j < NJ)  // every wave issues PER loads when NW divides NJ
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((char*)lds + 1024 * j), 16,
                                                  voff[k], 0, 0, 0);
     }
@@ -258,13 +141,13 @@ struct DmaSwz {
   // The caller orders every read of the target after an explicit vmcnt wait.
   __device__ __forceinline__ void issue_untracked(const bf16_t* base, int64_t ss, int64_t row0,
                                                   int64_t nrows, bf16_t* lds) const {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, ss, row0, nrows);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<T>(base, ss, row_bytes, row0, nrows);
     uint32_t a = (uint32_t)(uintptr_t)(lds_void*)lds;
     asm volatile("" : "+s"(a));
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = wave + k * NW;
-      if (j < NJ)
+      if (NJ % NW == 0 || j < NJ)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)(a + 1024 * j), 16,
                                                  voff[k], 0, 0, 0);
     }
