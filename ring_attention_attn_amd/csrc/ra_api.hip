@@ -77,7 +77,8 @@ ra_status ra_validate_step(const ra_step_desc* d, int32_t for_bwd) {
   if ((st = check_seg(d->k_nseg, d->k_seg_len, d->k_seg_pos)) != RA_OK) return st;
   const int64_t lq = (int64_t)d->q_nseg * d->q_seg_len;
   const int64_t lk = (int64_t)d->k_nseg * d->k_seg_len;
-  if (lq > (int64_t)1 << 31 || lk > (int64_t)1 << 31) return RA_EUNSUPPORTED;
+  // row counts, tile offsets and positions are int32 in the kernels
+  if (lq > INT32_MAX - 256 || lk > INT32_MAX - 256) return RA_EUNSUPPORTED;
   const int eb = elem_bytes(d->dtype);
   const int D = d->head_dim;
   if ((st = check_strides(d->q_ss, d->q_hs, lq, d->hq, D, eb)) != RA_OK) return st;

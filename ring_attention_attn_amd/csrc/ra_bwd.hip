@@ -269,8 +269,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   vst.init(p.v_ss, wave, lane);
   auto stage = [&](int t, auto b) {
     constexpr int B = decltype(b)::value;
-    kst.issue(K, p.k_ss, (int64_t)t * KT, lk, B ? sK1 : sK0);
-    vst.issue(V, p.v_ss, (int64_t)t * KT, lk, B ? sV1 : sV0);
+    kst.issue(K, t * KT, (int)lk, B ? sK1 : sK0);
+    vst.issue(V, t * KT, (int)lk, B ? sV1 : sV0);
   };
 
   // per-lane byte offsets in a swizzled tile: 16-byte row reads of chunk
@@ -468,9 +468,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   auto stage = [&](int hh, int t, auto b) {
     constexpr int B = decltype(b)::value;
     const int h = g * p.group + hh;
-    qst.issue((const bf16_t*)p.q + (int64_t)h * p.q_hs, p.q_ss, (int64_t)t * QT, lq, B ? sQ1 : sQ0);
-    gst.issue((const bf16_t*)p.dout + (int64_t)h * p.do_hs, p.do_ss, (int64_t)t * QT, lq,
-              B ? sG1 : sG0);
+    qst.issue((const bf16_t*)p.q + (int64_t)h * p.q_hs, t * QT, (int)lq, B ? sQ1 : sQ0);
+    gst.issue((const bf16_t*)p.dout + (int64_t)h * p.do_hs, t * QT, (int)lq, B ? sG1 : sG0);
   };
   // LSE and D of a tile: wave 0 loads them into registers one step before
   // they are written to LDS (at the start of the step before their tile's), so

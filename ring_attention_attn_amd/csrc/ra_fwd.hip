@@ -248,8 +248,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     return B == 0 ? sV0 : (B == 1 ? sV1 : sV2);
   };
   auto stage = [&](int t, auto b) {
-    kst.issue(K, p.k_ss, (int64_t)t * KT, lk, kbuf(b));
-    vst.issue(V, p.v_ss, (int64_t)t * KT, lk, vbuf(b));
+    kst.issue(K, t * KT, (int)lk, kbuf(b));
+    vst.issue(V, t * KT, (int)lk, vbuf(b));
   };
 
   // per-lane LDS offsets (elements); everything else is an immediate offset

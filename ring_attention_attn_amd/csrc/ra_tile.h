@@ -67,17 +67,22 @@ __device__ __forceinline__ float sum_halves(float x) {
 // 1024): lane i writes the 16 bytes at 1024 j + 16 i.
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Descriptor of the T-row tile starting at row0 of a tensor with nrows rows:
-// only rows that exist are in range. row_bytes = ss * 2; T * row_bytes < 2^31
-// (the host rejects larger strides), so the range is 32-bit arithmetic.
+// Descriptor of the T-row tile starting at row row0 of a tensor with nrows
+// rows: only rows that exist are in range. row_bytes = row stride in bytes; the
+// host keeps T * row_bytes and the row counts below 2^31, so the range and the
+// clamp are 32-bit arithmetic and the tile offset one 32 x 32 -> 64-bit product.
 template <int T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16_t* base, int64_t ss,
-                                                            uint32_t row_bytes, int64_t row0,
-                                                            int64_t nrows) {
-  const int64_t left = nrows - row0;
-  const int rows = left <= 0 ? 0 : (left >= T ? T : (int)left);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * ss), (short)0,
-                                           (int)(rows * row_bytes), 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16_t* base, uint32_t row_bytes,
+                                                            int row0, int nrows) {
+  // (all values are wave-uniform; readfirstlane keeps the descriptor in scalar
+  // registers, where the compiler would otherwise build a per-lane loop)
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  row_bytes = __builtin_amdgcn_readfirstlane(row_bytes);
+  const int left = __builtin_amdgcn_readfirstlane(nrows) - row0;
+  const int rows = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= T ? T : left));
+  const char* ptr = (const char*)base + (uint64_t)(uint32_t)row0 * row_bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0, (int)(rows * row_bytes),
+                                           0x00020000);
 }
 
 // ---- XOR-swizzled row-major tiles (no padding): rows of D bf16, 16-byte
@@ -123,32 +128,15 @@ struct DmaSwz {
       voff[k] = (uint32_t)(((int64_t)row * ss + 8 * c) * 2);
     }
   }
-  // tile rows [row0, row0 + T) of `base` (row stride ss elements) into `lds`
-  __device__ __forceinline__ void issue(const bf16_t* base, int64_t ss, int64_t row0,
-                                        int64_t nrows, bf16_t* lds) const {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<T>(base, ss, row_bytes, row0, nrows);
+  // tile rows [row0, row0 + T) of `base` (of nrows rows) into `lds`
+  __device__ __forceinline__ void issue(const bf16_t* base, int row0, int nrows,
+                                        bf16_t* lds) const {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<T>(base, row_bytes, row0, nrows);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = wave + k * NW;
       if (NJ % NW == 0 || j < NJ)  // every wave issues PER loads when NW divides NJ
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((char*)lds + 1024 * j), 16,
-                                                 voff[k], 0, 0, 0);
-    }
-  }
-  // Same, with the LDS destination passed as an opaque address: the compiler
-  // then does not tie later LDS reads to these loads (it would otherwise wait
-  // for them before reading a buffer it cannot tell apart from the target).
-  // The caller orders every read of the target after an explicit vmcnt wait.
-  __device__ __forceinline__ void issue_untracked(const bf16_t* base, int64_t ss, int64_t row0,
-                                                  int64_t nrows, bf16_t* lds) const {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<T>(base, ss, row_bytes, row0, nrows);
-    uint32_t a = (uint32_t)(uintptr_t)(lds_void*)lds;
-    asm volatile("" : "+s"(a));
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int j = wave + k * NW;
-      if (NJ % NW == 0 || j < NJ)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)(a + 1024 * j), 16,
                                                  voff[k], 0, 0, 0);
     }
   }
