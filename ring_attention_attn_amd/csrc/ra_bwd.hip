@@ -517,10 +517,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     const char* cG = (const char*)(B ? sG1 : sG0);
     sacc = f32x16{};
     pacc = f32x16{};
+    // the Q and dO row operands are read AH steps before their use, in a
+    // fixed issue order (each fence keeps the compiler from moving
+    // instructions across it), so the LDS latency hides behind the products
+    constexpr int AH = 3;
+    bf16x8 qa[AH + 1], ga[AH + 1];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) {
+      qa[i] = *(const bf16x8*)(cQ + (roff ^ (32 * i)));
+      ga[i] = *(const bf16x8*)(cG + (roff ^ (32 * i)));
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      sacc = mfma32(*(const bf16x8*)(cQ + (roff ^ (32 * c))), kreg[c], sacc);
-      pacc = mfma32(*(const bf16x8*)(cG + (roff ^ (32 * c))), vreg[c], pacc);
+      if (c + AH < NC) {
+        const int cn = c + AH < NC ? c + AH : 0;
+        qa[cn % (AH + 1)] = *(const bf16x8*)(cQ + (roff ^ (32 * cn)));
+        ga[cn % (AH + 1)] = *(const bf16x8*)(cG + (roff ^ (32 * cn)));
+      }
+      sacc = mfma32(qa[c % (AH + 1)], kreg[c], sacc);
+      pacc = mfma32(ga[c % (AH + 1)], vreg[c], pacc);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // register r is row 32 hf + 16 (r/8) + 8 hi + r%8 of the tile, the lane's key
     if (!qt_wg.mask_free(t)) {  // workgroup-uniform: one branch around branch-free selects
@@ -553,34 +569,46 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   };
   // phase 2: dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows, for
   // this wave's d half; chunk cq of rows is this wave's (registers) when
-  // cq / 2 == hf, else its partner's (LDS)
+  // cq / 2 == hf, else its partner's (LDS). Product m (of 8 NDH) is row chunk
+  // k = m / (2 NDH) (this wave's chunks first), d block db = (m / 2) % NDH and
+  // kind m % 2 (0: dV, 1: dK). Its A operand (dO^T or Q^T, read transposed)
+  // is read AHEAD products before its use, in a fixed issue order, so the LDS
+  // latency hides behind the products in flight.
   auto phase2 = [&](auto b) {
     constexpr int B = decltype(b)::value;
     // rows 32 hf' .. of the tile, hf' = the half of the chunk's owner
     const char* cQ = (const char*)(B ? sQ1 : sQ0);
     const char* cG = (const char*)(B ? sG1 : sG0);
     const int own_row = 32 * hf * 2 * D, partner_row = 32 * (hf ^ 1) * 2 * D;
+    constexpr int NM = 8 * NDH;
+    constexpr int AHEAD = 3;
+    auto a_op = [&](int m) -> bf16x8 {
+      const int k = m / (2 * NDH), db = (m / 2) % NDH;
+      const int rowb = (k < 2 ? own_row : partner_row) + 16 * (k & 1) * 2 * D;
+      const int dblk = 64 * (NDH * hf + db);  // byte XOR of the 32-wide d block
+      const char* a = ((m & 1) ? cQ : cG) + rowb;
+      return __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + (toff0 ^ dblk))),
+                                     ds_read_tr((const bf16_t*)(a + (toff1 ^ dblk))), 0, 1, 2,
+                                     3, 4, 5, 6, 7);
+    };
+    bf16x8 ar[AHEAD + 1];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int cc = k & 1;
-      const bool own = k < 2;  // this wave's chunks first: no LDS read for their B operand
-      const bf16x8 pb = own ? pk[cc] : *(const bf16x8*)(x_partner + (2 * cc) * 512);
-      const bf16x8 sb = own ? dsk[cc] : *(const bf16x8*)(x_partner + (2 * cc + 1) * 512);
-      const int rowb = (own ? own_row : partner_row) + 16 * cc * 2 * D;
+    for (int i = 0; i < AHEAD; ++i) ar[i] = a_op(i);
+    bf16x8 pb = pk[0], sb = dsk[0];
 #pragma unroll
-      for (int db = 0; db < NDH; ++db) {
-        const int dblk = 64 * (NDH * hf + db);  // byte XOR of the 32-wide d block
-        const char* ag = cG + rowb;
-        const char* aq = cQ + rowb;
-        const bf16x8 av = __builtin_shufflevector(ds_read_tr((const bf16_t*)(ag + (toff0 ^ dblk))),
-                                                  ds_read_tr((const bf16_t*)(ag + (toff1 ^ dblk))),
-                                                  0, 1, 2, 3, 4, 5, 6, 7);
-        dvacc[db] = mfma32(av, pb, dvacc[db]);
-        const bf16x8 aq8 = __builtin_shufflevector(ds_read_tr((const bf16_t*)(aq + (toff0 ^ dblk))),
-                                                   ds_read_tr((const bf16_t*)(aq + (toff1 ^ dblk))),
-                                                   0, 1, 2, 3, 4, 5, 6, 7);
-        dkacc[db] = mfma32(aq8, sb, dkacc[db]);
+    for (int m = 0; m < NM; ++m) {
+      const int k = m / (2 * NDH), db = (m / 2) % NDH;
+      if (m + AHEAD < NM) ar[(m + AHEAD) % (AHEAD + 1)] = a_op(m + AHEAD < NM ? m + AHEAD : 0);
+      if (m % (2 * NDH) == 0) {  // first product of a row chunk: its B operands
+        const int cc = k & 1;
+        pb = k < 2 ? pk[cc] : *(const bf16x8*)(x_partner + (2 * cc) * 512);
+        sb = k < 2 ? dsk[cc] : *(const bf16x8*)(x_partner + (2 * cc + 1) * 512);
       }
+      if ((m & 1) == 0)
+        dvacc[db] = mfma32(ar[m % (AHEAD + 1)], pb, dvacc[db]);
+      else
+        dkacc[db] = mfma32(ar[m % (AHEAD + 1)], sb, dkacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
