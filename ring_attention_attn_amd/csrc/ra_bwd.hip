@@ -274,19 +274,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   };
 
   // per-lane byte offsets in a swizzled tile: 16-byte row reads of chunk
-  // 2*c + hi of row kb*32 + sigma(l32), and transposing reads of rows
-  // 16*cc + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3)
-  int roff[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) roff[c] = swz_off<D>(srow, 2 * c + hi);
+  // 2*c + hi of row kb*32 + sigma(l32) (XOR 32 c), and transposing reads of
+  // rows 16*cc + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3)
+  // (XOR 64 db)
+  const int roff = swz_off<D>(srow, hi);
   const int grp = lane >> 4, gi = lane & 15;
-  int toff[2][ND];
-#pragma unroll
-  for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-      toff[sh][db] = swz_off<D>(8 * hi + (gi >> 2) + 4 * sh, 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1)) +
-                     8 * (gi & 1);
+  const int toff0 = swz_off<D>(8 * hi + (gi >> 2), 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  const int toff1 = swz_off<D>(8 * hi + (gi >> 2) + 4, 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
 
   auto compute = [&](int t, auto b) {
     constexpr int B = decltype(b)::value;
@@ -296,14 +290,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
     // S^T = K Q^T and dP^T = V dO^T; register r of key block kb is key
     // t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
     f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    // product i of 4 NC: step c = i / 4, key block kb = (i / 2) % 2, K (S) or
+    // V (dP) for i % 2; each A operand is read AH products ahead of its use, in
+    // a fixed issue order (each fence keeps the compiler from moving
+    // instructions across it), so the LDS latency hides behind the products
+    constexpr int NSD = 4 * NC, AH = 3;
+    auto sd_op = [&](int i) -> bf16x8 {
+      const int o = ((i / 2) % 2) * 32 * 2 * D + (roff ^ (32 * (i / 4)));
+      return *(const bf16x8*)(((i & 1) ? cV : cK) + o);
+    };
+    bf16x8 ar[AH + 1];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int i = 0; i < AH; ++i) ar[i] = sd_op(i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int o = kb * 32 * 2 * D + roff[c];
-        sacc[kb] = mfma32(*(const bf16x8*)(cK + o), qreg[c], sacc[kb]);
-        pacc[kb] = mfma32(*(const bf16x8*)(cV + o), doreg[c], pacc[kb]);
-      }
+    for (int i = 0; i < NSD; ++i) {
+      if (i + AH < NSD) ar[(i + AH) % (AH + 1)] = sd_op(i + AH < NSD ? i + AH : 0);
+      const int c = i / 4, kb = (i / 2) % 2;
+      if (i & 1)
+        pacc[kb] = mfma32(ar[i % (AH + 1)], doreg[c], pacc[kb]);
+      else
+        sacc[kb] = mfma32(ar[i % (AH + 1)], qreg[c], sacc[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (!kt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
       const TileRows tk(p.km, (int64_t)t * KT, KT);
       const MaskBounds mb(tk, qlim, 8 * hi, p.causal);
@@ -331,17 +339,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
         dsk[kb][hf] = pack_bf16x8(v);
       }
     // dQ^T += K^T dS^T: K^T operand = keys 16*cc + 8*hi .. +8 of d row
-    // 32*db + l32, read transposed; consecutive MFMAs use different accumulators
+    // 32*db + l32, read transposed, AH products ahead; product j of 4 ND is
+    // cc = j / ND, db = j % ND, so consecutive MFMAs use different accumulators
+    constexpr int NQ = 4 * ND;
+    auto kt_op = [&](int j) -> bf16x8 {
+      const char* a = cK + 16 * (j / ND) * 2 * D;
+      const int dblk = 64 * (j % ND);  // byte XOR of the 32-wide d block
+      return __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + (toff0 ^ dblk))),
+                                     ds_read_tr((const bf16_t*)(a + (toff1 ^ dblk))), 0, 1, 2,
+                                     3, 4, 5, 6, 7);
+    };
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+    for (int j = 0; j < AH; ++j) ar[j] = kt_op(j);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const char* a = cK + 16 * cc * 2 * D;
-        const bf16x4 lo4 = ds_read_tr((const bf16_t*)(a + toff[0][db]));
-        const bf16x4 hi4 = ds_read_tr((const bf16_t*)(a + toff[1][db]));
-        const bf16x8 ak = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        qacc[db] = mfma32(ak, dsk[cc >> 1][cc & 1], qacc[db]);
-      }
+    for (int j = 0; j < NQ; ++j) {
+      if (j + AH < NQ) ar[(j + AH) % (AH + 1)] = kt_op(j + AH < NQ ? j + AH : 0);
+      const int cc = j / ND, db = j % ND;
+      qacc[db] = mfma32(ar[j % (AH + 1)], dsk[cc >> 1][cc & 1], qacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   using B0 = std::integral_constant<int, 0>;
