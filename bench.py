@@ -206,6 +206,27 @@ class EventTimer:
         return float(np.sum([a.elapsed_time(b) for a, b in self.ev.get(kind, [])]))
 
 
+def gemm_reference(m=16384, n=16384, k=8192, reps=20):
+    """Rate of one large bf16 GEMM by the vendor library (torch.matmul ->
+    hipBLASLt) on this GPU, measured after the timed region: what a plain dense
+    contraction sustains here, a practical reference beside the nominal peak."""
+    import torch
+    a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"value": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+            "what": f"torch.matmul bf16 {m}x{n}x{k} (vendor GEMM), sustained on this GPU"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +245,8 @@ def main():
     ap.add_argument("--merge", choices=("fused", "separate"), default="fused",
                     help="fold each forward step into the running result in the forward "
                          "kernel (fused) or with a separate lse_merge launch")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the vendor-GEMM reference rate measured after the timed region")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one head_permute of 1 GiB (a plain copy of known size) before the "
                          "warmup, to calibrate HBM byte counters")
@@ -358,6 +381,8 @@ def main():
         perm_ms = timer.total_ms("head_permute") / args.steps
         out["breakdown_ms_per_step"] = {"head_permutes": round(perm_ms, 4)}
         out["head_permute_gbs"] = round(share.permute_bytes() / (perm_ms * 1e-3) / 1e9, 1)
+    if not args.no_gemm_ref:
+        out["gemm_ref"] = gemm_reference()
     if args.layout != "zigzag":
         log("cpu baseline is taken on the paired-block share only; skipped")
     elif not args.no_cpu_baseline:

@@ -23,7 +23,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline float to_f(bf16_t x) { return (float)x; }
+// the VALU kernels run the fp32 workload only
 __device__ inline float to_f(float x) { return x; }
 
 // ============================================================= VALU kernels

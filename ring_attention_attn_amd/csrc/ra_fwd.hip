@@ -30,16 +30,11 @@
 #include "ra_internal.h"
 #include "ra_tile.h"
 
-// explicit MFMA / vector instruction interleaving of the pipelined tile step
-#ifndef RA_FWD_SCHED
-#define RA_FWD_SCHED 1
-#endif
-
 namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
 
-__device__ inline float to_f(bf16_t x) { return (float)x; }
+// the VALU kernels run the fp32 workload only
 __device__ inline float to_f(float x) { return x; }
 
 // Fold a step's row (O_s, L_s) into the running (O_a, L_a), as the merge of
@@ -150,10 +145,44 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 // head. K and V tiles of 64 keys reach LDS by DMA into three rotating buffers
 // (one barrier per tile). The loop is software-pipelined: while the softmax and
 // O^T += V^T P^T of tile t run, the 16 MFMAs of S^T for the next tile are
-// issued in the same basic block, so vector and matrix work overlap inside
-// each wave. Tiles use the XOR-swizzled row layout: K rows are read with
-// 16-byte loads and V^T operands with ds_read_b64_tr_b16, both free of bank
-// conflicts. Diagonal tiles and ragged tails add one branch-free masking block.
+// issued in the same basic block, in a fixed order that interleaves them with
+// the O^T products and spreads the softmax between them, so vector and matrix
+// work overlap inside each wave. Tiles use the XOR-swizzled row layout: K rows
+// are read with 16-byte loads and V^T operands with ds_read_b64_tr_b16, both
+// free of bank conflicts. Diagonal tiles and ragged tails add one branch-free
+// masking block.
+
+// Issue order of a forward step with NS score products: four score products,
+// then O^T and score products alternating, then the remaining O^T products.
+// Returns the product at position pos: score product i (< NS) or NS + O^T product j.
+template <int NS>
+__host__ __device__ constexpr int prod_at(int pos) {
+  if (pos < 4) return pos;
+  const int k = pos - 4;
+  if (k < 2 * (NS - 4)) return (k % 2) ? 4 + k / 2 : NS + k / 2;
+  return NS + (NS - 4) + (k - 2 * (NS - 4));
+}
+template <int NS>
+__host__ __device__ constexpr int pos_of_o(int j) {
+  return j < NS - 4 ? 4 + 2 * j : 4 + 2 * (NS - 4) + (j - (NS - 4));
+}
+// position after which softmax element e (chunk e / 8 of 8 keys) is computed:
+// chunk k is spread over the positions before the first O^T product using it
+template <int NS, int ND>
+__host__ __device__ constexpr int elem_slot(int e) {
+  const int k = e / 8;
+  const int start = k == 0 ? 0 : pos_of_o<NS>((k - 1) * ND);
+  const int n = pos_of_o<NS>(k * ND) - start;
+  return start + ((e % 8) * n) / 8;
+}
+// two floats rounded to bf16 (round to nearest even) in one 32-bit register
+__device__ __forceinline__ uint32_t pk2_bf16(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
 template <int D, bool MERGE>
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
                                                           int rows_per_wg) {
@@ -256,17 +285,10 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   // per-lane byte offsets in a swizzled tile: 16-byte reads of chunk 2*c + hi
   // of row kb*32 + sigma(l32) (K), and transposing reads of rows
   // 16*cc + 8*hi + (gi / 4) (+4) at d = 32*db + 16*(grp & 1) + 4*(gi & 3) (V)
-  int koff[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) koff[c] = swz_off<D>(srow, 2 * c + hi);
+  const int roff = swz_off<D>(srow, hi);
   const int grp = lane >> 4, gi = lane & 15;
-  int voff[2][ND];
-#pragma unroll
-  for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-      voff[sh][db] = swz_off<D>(8 * hi + (gi >> 2) + 4 * sh, 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1)) +
-                     8 * (gi & 1);
+  const int toff0 = swz_off<D>(8 * hi + (gi >> 2), 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  const int toff1 = swz_off<D>(8 * hi + (gi >> 2) + 4, 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
 
   // S^T = K Q^T of the tile in buffer b; register r of key block kb is key
   // t*KT + kb*32 + 16*(r/8) + 8*hi + r%8
@@ -278,7 +300,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = mfma32(*(const bf16x8*)(cK + kb * 32 * 2 * D + koff[c]), qreg[c], sacc[kb]);
+        sacc[kb] = mfma32(*(const bf16x8*)(cK + kb * 32 * 2 * D + (roff ^ (32 * c))), qreg[c], sacc[kb]);
   };
   // mask scores of tile t for this wave's queries (keys past the end, and
   // causally later keys) and move the exponent shift if the tile needs it
@@ -317,67 +339,70 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
       for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
     }
   };
-  // P = exp2(S^T scale_log2 - m_run) in bf16, and O^T += V^T P^T from buffer b:
-  // the V^T operand is keys 16*cc + 8*hi .. +8 of d row 32*db + l32, read
-  // transposed from row-major V; consecutive MFMAs use different accumulators
-  auto accumulate = [&](auto b, const f32x16 (&sacc)[2]) {
+  // One step's products in a fixed issue order: the 2*NC score products of the
+  // next tile (A = K row chunk, one 16-byte read) and the 4*ND O^T products of
+  // this tile (A = V^T, two transposing reads) alternate after four score
+  // products; each A operand is read AH products ahead of its use, and the
+  // softmax of this tile (32 scores per lane in four chunks of 8 keys) is spread
+  // over the products before the first O^T product that needs each chunk.
+  // Fences keep the compiler from moving instructions across products, and the
+  // empty asm statements keep each softmax piece where it is placed (the
+  // instruction selector would otherwise sink it to its first use). Without the
+  // fixed order, the compiler read the V^T operands of two of the three unrolled
+  // steps right before their products and waited for each read.
+  constexpr int NS = 2 * NC, NO = 4 * ND, NPR = NS + NO, AH = 3;
+  auto block = [&](auto bc, auto bn, const f32x16 (&sacc)[2], f32x16 (&snew)[2]) {
+    const char* cK = (const char*)kbuf(bn);
+    const char* cV = (const char*)vbuf(bc);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 pk[2][2];
+    snew[0] = f32x16{};
+    snew[1] = f32x16{};
+    auto opnd = [&](int pos) -> bf16x8 {
+      const int pr = prod_at<NS>(pos);
+      if (pr < NS) return *(const bf16x8*)(cK + (pr % 2) * 32 * 2 * D + (roff ^ (32 * (pr / 2))));
+      const int j = pr - NS;
+      const char* a = cV + 16 * (j / ND) * 2 * D;
+      const int dblk = 64 * (j % ND);
+      return __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + (toff0 ^ dblk))),
+                                     ds_read_tr((const bf16_t*)(a + (toff1 ^ dblk))), 0, 1, 2, 3,
+                                     4, 5, 6, 7);
+    };
+    float pe[32];
+    uint32_t pw[16];
+    bf16x8 pkc[4];
     float rs0 = 0.f, rs1 = 0.f;
+    bf16x8 ar[AH + 1];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < AH; ++i) ar[i] = opnd(i);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float pe[8];
+    for (int pos = 0; pos < NPR; ++pos) {
+      if (pos + AH < NPR) ar[(pos + AH) % (AH + 1)] = opnd(pos + AH < NPR ? pos + AH : 0);
+      const int pr = prod_at<NS>(pos);
+      if (pr < NS) {
+        snew[pr % 2] = mfma32(ar[pos % (AH + 1)], qreg[pr / 2], snew[pr % 2]);
+      } else {
+        const int j = pr - NS;
+        oacc[j % ND] = mfma32(ar[pos % (AH + 1)], pkc[j / ND], oacc[j % ND]);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * hf + e], p.scale_log2, -m_use));
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
+      for (int e = 0; e < 32; ++e) {
+        if (elem_slot<NS, ND>(e) != pos) continue;
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e / 16][e % 16], p.scale_log2, -m_use));
+        if (e & 1) {
+          rs1 += pe[e];
+          pw[e / 2] = pk2_bf16(pe[e - 1], pe[e]);
+          asm volatile("" : "+v"(pw[e / 2]), "+v"(rs1));
+        } else {
           rs0 += pe[e];
-          rs1 += pe[e + 1];
+          asm volatile("" : "+v"(rs0));
         }
-        pk[kb][hf] = pack_bf16x8(pe);
+        if (e % 8 == 7)
+          pkc[e / 8] = __builtin_bit_cast(
+              bf16x8, u32x4{pw[e / 2 - 3], pw[e / 2 - 2], pw[e / 2 - 1], pw[e / 2]});
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     l_run += rs0 + rs1;
-    const char* cV = (const char*)vbuf(b);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const char* a = cV + 16 * cc * 2 * D;
-        const bf16x4 lo4 = ds_read_tr((const bf16_t*)(a + voff[0][db]));
-        const bf16x4 hi4 = ds_read_tr((const bf16_t*)(a + voff[1][db]));
-        const bf16x8 av = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = mfma32(av, pk[cc >> 1][cc & 1], oacc[db]);
-      }
-  };
-
-  // Issue order of the step's block: LDS reads run about six MFMAs ahead of
-  // their use; each of the 16 score MFMAs sits between four softmax vector
-  // instructions, each of the 16 O^T MFMAs between three.
-  auto interleave = [&]() {
-#if RA_FWD_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads: K for scores 0-5
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    }
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#endif
   };
 
   // One pipeline step. On entry sc holds the prepared scores of tile t (buffer
@@ -392,9 +417,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     __syncthreads();
     const int tn2 = tn < n_kt ? next_visible(tn + 1) : n_kt;
     if (tn2 < n_kt) stage(tn2, bn2);
-    scores(bn, sn);
-    accumulate(bc, sc);
-    interleave();
+    block(bc, bn, sc, sn);
     t = tn;
     tn = tn2;
     if (t < n_kt) {
