@@ -247,6 +247,8 @@ def main():
                          "kernel (fused) or with a separate lse_merge launch")
     ap.add_argument("--no-gemm-ref", action="store_true",
                     help="skip the vendor-GEMM reference rate measured after the timed region")
+    ap.add_argument("--gemm-ref-only", action="store_true",
+                    help="print only the vendor-GEMM reference rate (for counter runs of it)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one head_permute of 1 GiB (a plain copy of known size) before the "
                          "warmup, to calibrate HBM byte counters")
@@ -257,6 +259,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.gemm_ref_only:
+        print(json.dumps({"gemm_ref": gemm_reference()}), flush=True)
+        return
     from ring_attention_attn_amd import binding
     from ring_attention_attn_amd.configs import CONFIGS
     from ring_attention_attn_amd.ring import HeadParallelShare, ShareRing
