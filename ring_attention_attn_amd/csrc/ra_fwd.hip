@@ -304,8 +304,18 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   };
   // mask scores of tile t for this wave's queries (keys past the end, and
   // causally later keys) and move the exponent shift if the tile needs it
-  auto prepare = [&](int t, f32x16 (&sacc)[2]) {
-    if (!wave_active || !kt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
+  // max of 16 raw scores of a lane (a tree of depth 3)
+  auto max16 = [](const f32x16& v) {
+    const float a = fmax3(v[0], v[1], v[2]), b = fmax3(v[3], v[4], v[5]);
+    const float c = fmax3(v[6], v[7], v[8]), d = fmax3(v[9], v[10], v[11]);
+    const float e = fmax3(v[12], v[13], v[14]);
+    return __builtin_fmaxf(fmax3(a, b, c), fmax3(d, e, v[15]));
+  };
+  // mx_pre (have_pre): the lane's max of the tile's unmasked scores, computed
+  // in the step's block; tiles that need a mask recompute it after masking
+  auto prepare = [&](int t, f32x16 (&sacc)[2], float mx_pre, bool have_pre) {
+    const bool need_mask = !wave_active || !kt_w.mask_free(t);
+    if (need_mask) {  // wave-uniform: one branch around branch-free code
       // the lane part (8*hi) of each key offset is folded into the per-tile
       // bounds so each register compares against a constant
       const TileRows tk(p.km, (int64_t)t * KT, KT);
@@ -319,13 +329,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
         }
     }
     // tile row max on raw scores (scale > 0), over both lane halves
-    float mx = fmax3(sacc[0][0], sacc[0][1], sacc[0][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = fmax3(mx, sacc[0][r], sacc[0][r + 1]);
-    mx = fmax3(mx, sacc[0][15], sacc[1][0]);
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) mx = fmax3(mx, sacc[1][r], sacc[1][r + 1]);
-    mx = __builtin_fmaxf(mx, sacc[1][15]);
+    float mx = (have_pre && !need_mask) ? mx_pre : __builtin_fmaxf(max16(sacc[0]), max16(sacc[1]));
     mx = max_halves(mx);
     const float mt = mx * p.scale_log2;
     // the shift moves only when a row's max outgrows it by kThresh (rarely after
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   // fixed order, the compiler read the V^T operands of two of the three unrolled
   // steps right before their products and waited for each read.
   constexpr int NS = 2 * NC, NO = 4 * ND, NPR = NS + NO, AH = 3;
-  auto block = [&](auto bc, auto bn, const f32x16 (&sacc)[2], f32x16 (&snew)[2]) {
+  auto block = [&](auto bc, auto bn, const f32x16 (&sacc)[2], f32x16 (&snew)[2], float& mxo) {
     const char* cK = (const char*)kbuf(bn);
     const char* cV = (const char*)vbuf(bc);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
                                      ds_read_tr((const bf16_t*)(a + (toff1 ^ dblk))), 0, 1, 2, 3,
                                      4, 5, 6, 7);
     };
-    float pe[32];
+    float pe[32], mx0 = 0.f;
     uint32_t pw[16];
     bf16x8 pkc[4];
     float rs0 = 0.f, rs1 = 0.f;
@@ -400,6 +404,16 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
           pkc[e / 8] = __builtin_bit_cast(
               bf16x8, u32x4{pw[e / 2 - 3], pw[e / 2 - 2], pw[e / 2 - 1], pw[e / 2]});
       }
+      // the lane's max of the new (unmasked) scores, among the last O^T products,
+      // once the score products have completed: off the path to the next step
+      if (pos == NPR - 3) {
+        mx0 = max16(snew[0]);
+        asm volatile("" : "+v"(mx0));
+      }
+      if (pos == NPR - 2) {
+        mxo = __builtin_fmaxf(mx0, max16(snew[1]));
+        asm volatile("" : "+v"(mxo));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += rs0 + rs1;
@@ -417,13 +431,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     __syncthreads();
     const int tn2 = tn < n_kt ? next_visible(tn + 1) : n_kt;
     if (tn2 < n_kt) stage(tn2, bn2);
-    block(bc, bn, sc, sn);
+    float mxn = 0.f;
+    block(bc, bn, sc, sn, mxn);
     t = tn;
     tn = tn2;
     if (t < n_kt) {
       sc[0] = sn[0];
       sc[1] = sn[1];
-      prepare(t, sc);
+      prepare(t, sc, mxn, true);
     }
     return t < n_kt;
   };
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     wait_vmem();
     __syncthreads();
     scores(B0{}, sc);
-    prepare(t, sc);
+    prepare(t, sc, 0.f, false);
     // buffers rotate 0 -> 1 -> 2; unrolled so each buffer is a distinct array
     // (the compiler then knows a DMA into one does not alias reads of another)
     while (step(B0{}, B1{}, B2{}) && step(B1{}, B2{}, B0{}) && step(B2{}, B0{}, B1{})) {
