@@ -142,8 +142,8 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(StepParams p) {
 
 // ============================================================= MFMA kernel
 // A workgroup is 8 waves (two per SIMD); wave w owns 32 query rows of one query
-// head. K and V tiles of 64 keys reach LDS by DMA into three rotating buffers
-// (one barrier per tile). The loop is software-pipelined: while the softmax and
+// head. K and V tiles of 64 keys reach LDS by DMA, two buffers each (one
+// barrier per tile). The loop is software-pipelined: while the softmax and
 // O^T += V^T P^T of tile t run, the 16 MFMAs of S^T for the next tile are
 // issued in the same basic block, in a fixed order that interleaves them with
 // the O^T products and spreads the softmax between them, so vector and matrix
@@ -195,10 +195,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   constexpr float kThresh = 8.f;
   __shared__ __attribute__((aligned(1024))) bf16_t sK0[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sK1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sK2[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sV0[TB];
   __shared__ __attribute__((aligned(1024))) bf16_t sV1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV2[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,10 +230,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   for (int i = tid; i < TB / 8; i += NW * 64) {
     ((bf16x8*)sK0)[i] = bf16x8{};
     ((bf16x8*)sK1)[i] = bf16x8{};
-    ((bf16x8*)sK2)[i] = bf16x8{};
     ((bf16x8*)sV0)[i] = bf16x8{};
     ((bf16x8*)sV1)[i] = bf16x8{};
-    ((bf16x8*)sV2)[i] = bf16x8{};
   }
 
   // Q^T as the B operand: lane holds query column l32, d = 16c + 8*hi .. +8
@@ -270,16 +266,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   vst.init(p.v_ss, wave, lane);
   auto kbuf = [&](auto b) -> bf16_t* {
     constexpr int B = decltype(b)::value;
-    return B == 0 ? sK0 : (B == 1 ? sK1 : sK2);
+    return B == 0 ? sK0 : sK1;
   };
   auto vbuf = [&](auto b) -> bf16_t* {
     constexpr int B = decltype(b)::value;
-    return B == 0 ? sV0 : (B == 1 ? sV1 : sV2);
+    return B == 0 ? sV0 : sV1;
   };
-  auto stage = [&](int t, auto b) {
-    kst.issue(K, t * KT, (int)lk, kbuf(b));
-    vst.issue(V, t * KT, (int)lk, vbuf(b));
-  };
+  auto stage_k = [&](int t, auto b) { kst.issue(K, t * KT, (int)lk, kbuf(b)); };
+  auto stage_v = [&](int t, auto b) { vst.issue(V, t * KT, (int)lk, vbuf(b)); };
 
   // per-lane LDS offsets (elements); everything else is an immediate offset
   // per-lane byte offsets in a swizzled tile: 16-byte reads of chunk 2*c + hi
@@ -419,20 +413,25 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     l_run += rs0 + rs1;
   };
 
-  // One pipeline step. On entry sc holds the prepared scores of tile t (buffer
-  // bc) and the DMA of tile tn (buffer bn) is in flight. The barrier makes tn
-  // visible and frees bn2 (last read one step ago) for the DMA of the tile after
-  // tn. Scores of tn are computed (unconditionally: past the end they are
-  // discarded) in the same block as tile t's softmax and O update.
+  // One pipeline step. On entry sc holds the prepared scores of tile t, whose V
+  // is in buffer bv, and the K of the next tile tn is in bk. K and V rotate
+  // through two buffers each: after the barrier (which makes the previous
+  // step's loads visible and ends all reads of that step) the K of the tile
+  // after tn goes into bkl (tile t's K buffer) and the V of tn into bvl (the
+  // V buffer read one step ago). Scores of tn are computed (unconditionally:
+  // past the end they are discarded) in the same block as tile t's softmax and
+  // O update; the loop is unrolled so each buffer is a distinct array (the
+  // compiler then knows a load into one does not alias reads of another).
   f32x16 sc[2], sn[2];
   int t = next_visible(0), tn = n_kt;
-  auto step = [&](auto bc, auto bn, auto bn2) {
+  auto step = [&](auto bv, auto bk, auto bkl, auto bvl) {
     wait_vmem();
     __syncthreads();
     const int tn2 = tn < n_kt ? next_visible(tn + 1) : n_kt;
-    if (tn2 < n_kt) stage(tn2, bn2);
+    if (tn2 < n_kt) stage_k(tn2, bkl);
+    if (tn < n_kt) stage_v(tn, bvl);
     float mxn = 0.f;
-    block(bc, bn, sc, sn, mxn);
+    block(bv, bk, sc, sn, mxn);
     t = tn;
     tn = tn2;
     if (t < n_kt) {
@@ -447,17 +446,15 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   if (t < n_kt) {
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    using B2 = std::integral_constant<int, 2>;
-    stage(t, B0{});
+    stage_k(t, B0{});
+    stage_v(t, B0{});
     tn = next_visible(t + 1);
-    if (tn < n_kt) stage(tn, B1{});
+    if (tn < n_kt) stage_k(tn, B1{});
     wait_vmem();
     __syncthreads();
     scores(B0{}, sc);
     prepare(t, sc, 0.f, false);
-    // buffers rotate 0 -> 1 -> 2; unrolled so each buffer is a distinct array
-    // (the compiler then knows a DMA into one does not alias reads of another)
-    while (step(B0{}, B1{}, B2{}) && step(B1{}, B2{}, B0{}) && step(B2{}, B0{}, B1{})) {
+    while (step(B0{}, B1{}, B0{}, B1{}) && step(B1{}, B0{}, B1{}, B0{})) {
     }
   }
 
