@@ -184,8 +184,8 @@ ra_status ra_bwd_delta(int64_t rows, int32_t hq, int32_t head_dim, int32_t dtype
  *               src[t][q*(h/p) + j][x] (destination q receives head group q);
  * inverse == 1: the exact inverse (src is [p][s][h/p][d]).
  * A bit copy of elem_bytes (2 or 4) wide elements; both contiguous;
- * requires h % p == 0 and (h/p)*d*elem_bytes a multiple of 16. src and dst
- * must not overlap.
+ * requires h % p == 0 and (h/p)*d*elem_bytes a multiple of 16 (RA_EALIGN
+ * otherwise). src and dst must not overlap. p > 65535 returns RA_EUNSUPPORTED.
  */
 ra_status head_permute(const void* src, void* dst, int64_t s, int32_t h, int32_t d,
                        int32_t p, int32_t elem_bytes, int32_t inverse,

@@ -200,6 +200,7 @@ ra_status head_permute(const void* src, void* dst, int64_t s, int32_t h, int32_t
   if (elem_bytes_ != 2 && elem_bytes_ != 4) return RA_EINVAL;
   if (inverse != 0 && inverse != 1) return RA_EINVAL;
   if (h % p != 0) return RA_EINVAL;  // every destination needs whole heads
+  if (p > 65535) return RA_EUNSUPPORTED;  // one grid row per head group
   if (((int64_t)(h / p) * d * elem_bytes_) % 16 != 0) return RA_EALIGN;
   if (s == 0) return RA_OK;
   if (!src || !dst) return RA_EINVAL;

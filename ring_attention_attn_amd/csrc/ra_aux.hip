@@ -2,6 +2,7 @@
 // the backward preprocess D = rowsum(dO * O) (+ bf16 cast of O), the local head
 // permute of the head-parallel all-to-all, and a fill. All are HBM-bound: each
 // lane moves 16-byte vectors along the contiguous head_dim axis.
+#include <limits.h>
 #include <math.h>
 
 #include "ra_internal.h"
@@ -108,24 +109,28 @@ __global__ __launch_bounds__(kBlock) void bwd_delta_kernel(int64_t rows, int32_t
 }
 
 // ---------------------------------------------------------------- head permute
-// A copy of s*p contiguous runs of R bytes: run (q, t) of the [p][s][h/p][d]
-// side is run (t, q) of the [s][h][d] side. 16-byte vectors, grid-stride.
-__global__ __launch_bounds__(kBlock) void head_permute_kernel(const uint4* __restrict__ src,
-                                                              uint4* __restrict__ dst, int64_t s,
-                                                              int32_t p, int64_t run16,
-                                                              int32_t inverse) {
-  const int64_t total = s * p * run16;
-  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * kBlock) {
-    // t indexes the [p][s] side (grouped) when writing forward, reading inverse
-    const int64_t run = t / run16, off = t % run16;
-    const int64_t q = run / s, tok = run % s;
-    const int64_t flat = (tok * p + q) * run16 + off;  // same vector on the [s][h] side
-    if (!inverse)
-      dst[t] = src[flat];
-    else
-      dst[flat] = src[t];
-  }
+// A copy of s*p contiguous runs of run16 16-byte vectors: run (q, t) of the
+// [p][s][h/p][d] side is run (t, q) of the [s][h][d] side. Block (x, q) copies
+// the runs of group q for tokens x*rpb .. x*rpb + rpb - 1 (rpb = runs per
+// block), one vector per thread (runs longer than a block loop), so the index
+// arithmetic is a few integer operations per thread; every byte is read and
+// written once, with non-temporal hints.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(kBlock) void head_permute_kernel(const i32x4* __restrict__ src,
+                                                              i32x4* __restrict__ dst, int64_t s,
+                                                              int32_t p, int32_t run16,
+                                                              int32_t rpb, int32_t inverse) {
+  const int q = blockIdx.y;
+  const int lr = rpb > 1 ? (int)threadIdx.x / run16 : 0;
+  if (lr >= rpb) return;
+  const int64_t tok = (int64_t)blockIdx.x * rpb + lr;
+  if (tok >= s) return;
+  const int64_t grouped = ((int64_t)q * s + tok) * run16;  // [p][s] side
+  const int64_t flat = (tok * p + q) * run16;             // [s][h] side
+  const i32x4* from = src + (inverse ? grouped : flat);
+  i32x4* to = dst + (inverse ? flat : grouped);
+  for (int off = (int)threadIdx.x - lr * run16; off < run16; off += kBlock)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(from + off), to + off);
 }
 
 __global__ __launch_bounds__(kBlock) void fill_kernel(float* __restrict__ dst, int64_t n, float v) {
@@ -176,10 +181,12 @@ hipError_t launch_bwd_delta(int64_t rows, int32_t hq, int32_t d, int32_t dtype, 
 hipError_t launch_head_permute(const void* src, void* dst, int64_t s, int32_t h, int32_t d,
                                int32_t p, int32_t elem_bytes, int32_t inverse, hipStream_t st) {
   const int64_t run16 = (int64_t)(h / p) * d * elem_bytes / 16;
-  const int64_t total = s * p * run16;
-  const unsigned g = grid_for(total, kBlock * 8, 16384);
-  hipLaunchKernelGGL(head_permute_kernel, dim3(g), dim3(kBlock), 0, st, (const uint4*)src,
-                     (uint4*)dst, s, p, run16, inverse);
+  if (run16 > INT32_MAX) return hipErrorInvalidValue;
+  const int32_t rpb = run16 >= kBlock ? 1 : (int32_t)(kBlock / run16);
+  const int64_t gx = (s + rpb - 1) / rpb;
+  if (gx > INT32_MAX || p > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(head_permute_kernel, dim3((unsigned)gx, (unsigned)p), dim3(kBlock), 0, st,
+                     (const i32x4*)src, (i32x4*)dst, s, p, (int32_t)run16, rpb, inverse);
   return hipGetLastError();
 }
 

@@ -154,6 +154,8 @@ def test_calls_reject_before_device_work():
         (lambda: B.head_permute(16, 4096, 8, 8, 4, 8, 2, stream=0), B.RA_EALIGN),     # 8-byte runs
         (lambda: B.head_permute(16, 32, 8, 8, 128, 4, 2, stream=0), B.RA_EINVAL),     # overlap
         (lambda: B.head_permute(16, 1 << 20, 8, 8, 128, 4, 3, stream=0), B.RA_EINVAL),
+        (lambda: B.head_permute(16, 1 << 30, 8, 65536, 8, 65536, 2, stream=0),     # p > 65535
+         B.RA_EUNSUPPORTED),
         (lambda: B.ra_fill_f32(8, 10, 0.0, stream=0), B.RA_EALIGN),
         (lambda: B.ra_fill_f32(16, -1, 0.0, stream=0), B.RA_EINVAL),
     ]:

@@ -72,7 +72,9 @@ def _guards_checked():
 # ------------------------------------------------------------------ head permute
 
 @pytest.mark.parametrize("s,h,d,p,eb", [(37, 8, 128, 4, 2), (64, 32, 128, 4, 2), (5, 6, 16, 3, 4),
-                                        (100, 8, 64, 8, 2), (16, 4, 128, 1, 2)])
+                                        (100, 8, 64, 8, 2), (16, 4, 128, 1, 2),
+                                        (97, 9, 16, 3, 2),     # 6-vector runs: 42 runs per block
+                                        (3, 32, 128, 1, 4)])   # 1024-vector runs: a block loops
 def test_head_permute_bit_exact(s, h, d, p, eb):
     rng = np.random.default_rng(s + h)
     dt = np.uint16 if eb == 2 else np.uint32
