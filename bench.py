@@ -242,7 +242,7 @@ def main():
     ap.add_argument("--kv-rings", choices=("one", "ab"), default="one",
                     help="one launch per ring step, or two (one per block of the KV chunk: "
                          "the block A and block B rings)")
-    ap.add_argument("--merge", choices=("fused", "separate"), default="fused",
+    ap.add_argument("--merge", choices=("fused", "separate", "chunks"), default="fused",
                     help="fold each forward step into the running result in the forward "
                          "kernel (fused) or with a separate lse_merge launch")
     ap.add_argument("--no-gemm-ref", action="store_true",
@@ -318,7 +318,7 @@ def main():
     value = total * args.steps / wall / 1e12
 
     from ring_attention_attn_amd import binding as B
-    if args.merge == "fused":
+    if args.merge in ("fused", "chunks"):
         # the merge runs inside the forward launches; time the standalone kernel
         # (outside the timed steps, over all rows) for its own bandwidth figure
         ring.o_step.zero_()
@@ -341,7 +341,8 @@ def main():
     # (2b^2 per head per step, +b on the diagonal step); averaged over the P launches
     n_launch = len(ring.launches)   # P, or 2P with the block A / block B rings
     bwd_launch_flops = bwd_flops / n_launch
-    fwd_launch_flops = fwd_flops / n_launch
+    # with --merge chunks the forward is one launch over all steps
+    fwd_launch_flops = fwd_flops if args.merge == "chunks" else fwd_flops / n_launch
     bwd_tflops = bwd_launch_flops / (bwd_ms * 1e-3) / 1e12
     fwd_tflops = fwd_launch_flops / (fwd_ms * 1e-3) / 1e12
     merge_bytes = merge_rows * cfg.hq * (cfg.d * 4 * 3 + 4 * 3)

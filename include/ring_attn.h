@@ -120,6 +120,28 @@ ra_status ring_attn_step_fwd_merge(const ra_step_desc* desc, const void* q, cons
                                    ra_stream_t stream);
 
 /*
+ * ring_attn_fwd_chunks -- the forward of all n ring steps of this share in one
+ * launch: ring_attn_step_fwd of chunk 0 folded with chunks 1 .. n-1 as
+ * ring_attn_step_fwd_merge folds them ("Guide to LoongTrain", "The
+ * Communication Overhead and Causal Imbalance of Ring Attention": each rank
+ * attends its queries to every KV chunk), for a GPU that holds every chunk (the
+ * one-GPU virtual ring). The running max, sum and output stay in registers from
+ * one chunk to the next and O, LSE are written once, so no partial result goes
+ * through memory; the softmax is the same, its rounding differs from the
+ * per-step path's (no intermediate normalisation).
+ * descs: n descriptors, chunk i's key side in descs[i]; every other field
+ * (dtype, head_dim, heads, query segments, causal, scale, q/k/v/o strides)
+ * must equal descs[0]'s (RA_EINVAL otherwise). k, v: host arrays of n device
+ * pointers (chunk i's K and V). o: fp32 [lq][hq][d] (descs[0]'s o strides),
+ * lse: fp32 [hq][lq], both written (rows with no visible key anywhere: O = 0,
+ * LSE = -inf). 1 <= n <= 32 (RA_EUNSUPPORTED beyond); bf16 only
+ * (RA_EUNSUPPORTED for fp32). Chunks with lk == 0 are skipped.
+ */
+ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,
+                               const void* const* k, const void* const* v, float* o,
+                               float* lse, ra_stream_t stream);
+
+/*
  * ring_attn_step_bwd -- one step's share of the attention gradient, driven by
  * the FINAL log-sum-exp and D of the rows (saved-LSE recompute).
  *

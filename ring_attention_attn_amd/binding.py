@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EALIGN, RA_EDEVICE = 0, 1, 2, 3, 4
 RA_BF16, RA_F32 = 0, 1
 
-EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_fwd_merge", "ring_attn_step_bwd", "lse_merge",
+EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_fwd_merge", "ring_attn_fwd_chunks",
+           "ring_attn_step_bwd", "lse_merge",
            "ra_bwd_delta",
            "head_permute", "ra_fill_f32", "ra_zigzag_positions", "ra_zigzag_segments",
            "ra_double_ring_order", "ra_validate_step", "ra_status_str")
@@ -64,6 +65,7 @@ def lib():
         sig = {
             "ring_attn_step_fwd": [pd, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_fwd_merge": [pd, vp, vp, vp, vp, vp, vp],
+            "ring_attn_fwd_chunks": [pd, i32, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_bwd": [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "lse_merge": [i64, i32, i32, i64, i64, vp, vp, vp, vp, vp],
             "ra_bwd_delta": [i64, i32, i32, i32, vp, vp, vp, vp, vp],
@@ -174,6 +176,21 @@ def ring_attn_step_fwd_merge(desc, q, k, v, o_acc, lse_acc, stream=None):
     _check(lib().ring_attn_step_fwd_merge(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(o_acc), _ptr(lse_acc), _stream(stream)),
            "ring_attn_step_fwd_merge")
+
+
+def ring_attn_fwd_chunks(descs, q, ks, vs, o, lse, stream=None):
+    """All ring steps of the forward in one launch: descs, ks, vs are sequences
+    (chunk i's descriptor, K and V); o, lse are written."""
+    n = len(descs)
+    if len(ks) != n or len(vs) != n:
+        raise ValueError("ring_attn_fwd_chunks: descs, ks and vs must have the same length")
+    arr = (RaStepDesc * max(n, 1))(*descs)
+    for d, k, v in zip(descs, ks, vs):
+        _step_args(d, 0, q, k, v, o, lse)
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(k) for k in ks])
+    vp_ = (ctypes.c_void_p * max(n, 1))(*[_ptr(v) for v in vs])
+    _check(lib().ring_attn_fwd_chunks(arr, n, _ptr(q), kp, vp_, _ptr(o), _ptr(lse),
+                                      _stream(stream)), "ring_attn_fwd_chunks")
 
 
 def ring_attn_step_bwd(desc, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, stream=None):

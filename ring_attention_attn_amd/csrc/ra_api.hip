@@ -144,6 +144,52 @@ ra_status ring_attn_step_fwd_merge(const ra_step_desc* d, const void* q, const v
   return from_hip(launch_step_fwd(p, d->dtype, d->head_dim, (hipStream_t)stream));
 }
 
+// the query side, the key/value strides and the scale of every chunk's
+// descriptor must be those of the first
+static bool same_query_side(const ra_step_desc* a, const ra_step_desc* b) {
+  if (a->dtype != b->dtype || a->head_dim != b->head_dim || a->hq != b->hq || a->hkv != b->hkv)
+    return false;
+  if (a->q_nseg != b->q_nseg || a->q_seg_len != b->q_seg_len) return false;
+  for (int i = 0; i < a->q_nseg; ++i)
+    if (a->q_seg_pos[i] != b->q_seg_pos[i]) return false;
+  return a->causal == b->causal && a->scale == b->scale && a->q_ss == b->q_ss &&
+         a->q_hs == b->q_hs && a->k_ss == b->k_ss && a->k_hs == b->k_hs && a->v_ss == b->v_ss &&
+         a->v_hs == b->v_hs && a->o_ss == b->o_ss && a->o_hs == b->o_hs;
+}
+
+ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,
+                               const void* const* k, const void* const* v, float* o, float* lse,
+                               ra_stream_t stream) {
+  if (!descs || n < 1 || !k || !v) return RA_EINVAL;
+  if (n > kMaxChunks) return RA_EUNSUPPORTED;
+  for (int i = 0; i < n; ++i) {
+    const ra_status st = ra_validate_step(&descs[i], 0);
+    if (st != RA_OK) return st;
+    if (!same_query_side(&descs[0], &descs[i])) return RA_EINVAL;
+  }
+  const ra_step_desc* d0 = &descs[0];
+  if (d0->dtype != RA_BF16) return RA_EUNSUPPORTED;  // the MFMA kernels only
+  const int64_t lq = (int64_t)d0->q_nseg * d0->q_seg_len;
+  if (lq == 0) return RA_OK;
+  if (!q || !o || !lse) return RA_EINVAL;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lse)) return RA_EALIGN;
+  FwdChunks ch;
+  memset(&ch, 0, sizeof(ch));
+  for (int i = 0; i < n; ++i) {
+    const ra_step_desc* d = &descs[i];
+    if ((int64_t)d->k_nseg * d->k_seg_len == 0) continue;  // an empty chunk adds nothing
+    if (!k[i] || !v[i]) return RA_EINVAL;
+    if (!aligned16(k[i]) || !aligned16(v[i])) return RA_EALIGN;
+    ch.k[ch.n] = k[i];
+    ch.v[ch.n] = v[i];
+    ch.km[ch.n] = make_map(d->k_nseg, d->k_seg_len, d->k_seg_pos);
+    ++ch.n;
+  }
+  StepParams p = make_params(d0);
+  p.q = q; p.o = o; p.lse_out = lse;
+  return from_hip(launch_fwd_chunks(p, ch, d0->head_dim, (hipStream_t)stream));
+}
+
 ra_status ring_attn_step_bwd(const ra_step_desc* d, const void* q, const void* k, const void* v,
                              const void* dout, const float* lse, const float* delta,
                              float* dq_acc, float* dk_acc, float* dv_acc, ra_stream_t stream) {

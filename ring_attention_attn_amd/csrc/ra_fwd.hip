@@ -183,9 +183,12 @@ __device__ __forceinline__ uint32_t pk2_bf16(float a, float b) {
 }
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
-template <int D, bool MERGE>
-__global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
-                                                          int rows_per_wg) {
+// The body of the step kernels. MULTI: the whole ring in one launch, chunk c
+// of ch in turn (K, V and key map per chunk), the running max, sum and output
+// carried in registers from one chunk to the next and written once at the end.
+template <int D, bool MERGE, bool MULTI>
+__device__ __forceinline__ void fwd_mfma_body(const StepParams& p, int hpw, int n_qt,
+                                              int rows_per_wg, const FwdChunks* ch) {
   constexpr int NW = 8;            // waves per workgroup
   constexpr int KT = 64;           // keys per LDS tile
   constexpr int TB = KT * D;       // elements per K / V tile (XOR-swizzled rows, no padding)
@@ -213,7 +216,9 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   const int qt = n_qt - 1 - (logical % n_qt);
   const int g = gh / nsub, hs = gh % nsub;
   const int h = g * p.group + hs * hpw + (wave % hpw);
-  const int64_t lq = p.qm.len, lk = p.km.len;
+  const int64_t lq = p.qm.len;
+  SegMap km = MULTI ? ch->km[0] : p.km;  // key map of the chunk being processed
+  int64_t lk = km.len;
   const int64_t wg_r0 = (int64_t)qt * rows_per_wg;
   const int64_t row0 = wg_r0 + (int64_t)(wave / hpw) * 32;
 
@@ -222,8 +227,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   if (wave_active) seg_bounds(p.qm, row0, row0 + 32 < lq ? row0 + 32 : lq, wq_lo, wq_hi);
   seg_bounds(p.qm, wg_r0, wg_r0 + rows_per_wg < lq ? wg_r0 + rows_per_wg : lq, gq_lo, gq_hi);
 
-  const bf16_t* K = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
-  const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
+  const bf16_t* K = (const bf16_t*)(MULTI ? ch->k[0] : p.k) + (int64_t)g * p.k_hs;
+  const bf16_t* V = (const bf16_t*)(MULTI ? ch->v[0] : p.v) + (int64_t)g * p.v_hs;
 
   // stale LDS must hold finite values: keys past the end are never read into
   // P != 0, but 0 * NaN would poison O
@@ -256,9 +261,9 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   float l_run = 0.f;        // running sum of this half-wave's keys
 
   // visible key tiles of the workgroup, and the tiles this wave must mask
-  const KeyTiles<KT> kt_wg(p.km, p.causal, gq_lo, gq_hi);
-  const KeyTiles<KT> kt_w(p.km, p.causal, wq_lo, wq_hi);
-  const int n_kt = kt_wg.n;
+  KeyTiles<KT> kt_wg(km, p.causal, gq_lo, gq_hi);
+  KeyTiles<KT> kt_w(km, p.causal, wq_lo, wq_hi);
+  int n_kt = kt_wg.n;
   auto next_visible = [&](int t) { return kt_wg.next(t); };
 
   DmaSwz<KT, D, NW, MERGE ? 5 : 0> kst, vst;
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
     if (need_mask) {  // wave-uniform: one branch around branch-free code
       // the lane part (8*hi) of each key offset is folded into the per-tile
       // bounds so each register compares against a constant
-      const TileRows tk(p.km, (int64_t)t * KT, KT);
+      const TileRows tk(km, (int64_t)t * KT, KT);
       const MaskBounds mb(tk, qlim, 8 * hi, p.causal);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -443,18 +448,33 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   };
 
   __syncthreads();  // zero-fill done before any DMA lands
-  if (t < n_kt) {
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    stage_k(t, B0{});
-    stage_v(t, B0{});
-    tn = next_visible(t + 1);
-    if (tn < n_kt) stage_k(tn, B1{});
-    wait_vmem();
-    __syncthreads();
-    scores(B0{}, sc);
-    prepare(t, sc, 0.f, false);
-    while (step(B0{}, B1{}, B0{}, B1{}) && step(B1{}, B0{}, B1{}, B0{})) {
+  const int n_chunks = MULTI ? ch->n : 1;
+  for (int c = 0; c < n_chunks; ++c) {
+    if (MULTI && c > 0) {
+      km = ch->km[c];
+      lk = km.len;
+      K = (const bf16_t*)ch->k[c] + (int64_t)g * p.k_hs;
+      V = (const bf16_t*)ch->v[c] + (int64_t)g * p.v_hs;
+      kt_wg = KeyTiles<KT>(km, p.causal, gq_lo, gq_hi);
+      kt_w = KeyTiles<KT>(km, p.causal, wq_lo, wq_hi);
+      n_kt = kt_wg.n;
+      t = next_visible(0);
+      tn = n_kt;
+      __syncthreads();  // every wave is done with the previous chunk's buffers
+    }
+    if (t < n_kt) {
+      using B0 = std::integral_constant<int, 0>;
+      using B1 = std::integral_constant<int, 1>;
+      stage_k(t, B0{});
+      stage_v(t, B0{});
+      tn = next_visible(t + 1);
+      if (tn < n_kt) stage_k(tn, B1{});
+      wait_vmem();
+      __syncthreads();
+      scores(B0{}, sc);
+      prepare(t, sc, 0.f, false);
+      while (step(B0{}, B1{}, B0{}, B1{}) && step(B1{}, B0{}, B1{}, B0{})) {
+      }
     }
   }
 
@@ -498,6 +518,18 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
   }
 }
 
+template <int D, bool MERGE>
+__global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw, int n_qt,
+                                                          int rows_per_wg) {
+  fwd_mfma_body<D, MERGE, false>(p, hpw, n_qt, rows_per_wg, nullptr);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void fwd_chunks_kernel(StepParams p, int hpw, int n_qt,
+                                                            int rows_per_wg, FwdChunks ch) {
+  fwd_mfma_body<D, false, true>(p, hpw, n_qt, rows_per_wg, &ch);
+}
+
 int gcd_int(int a, int b) {
   while (b) {
     int t = a % b;
@@ -523,6 +555,18 @@ hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_chunks(const StepParams& p, const FwdChunks& ch, hipStream_t s) {
+  const int hpw = gcd_int(p.group, 4);
+  const int rows_per_wg = (8 / hpw) * 32;
+  const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
+  const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_chunks_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw, n_qt,
+                     rows_per_wg, ch);
+  return hipGetLastError();
+}
+
 template <int D, typename T>
 hipError_t launch_simple(const StepParams& p, hipStream_t s) {
   constexpr int RPB = 64 / (D / 64);
@@ -535,6 +579,11 @@ hipError_t launch_simple(const StepParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_fwd_chunks(const StepParams& p, const FwdChunks& ch, int head_dim,
+                             hipStream_t s) {
+  return head_dim == 128 ? launch_chunks<128>(p, ch, s) : launch_chunks<64>(p, ch, s);
+}
 
 hipError_t launch_step_fwd(const StepParams& p, int dtype, int head_dim, hipStream_t s) {
   if (dtype == RA_BF16) {

@@ -58,9 +58,22 @@ struct StepParams {
   float scale_log2;        // scale * log2(e)
 };
 
+// The key-side inputs of every ring step, for the forward that runs the whole
+// ring in one launch (bf16 only); the query side and the strides are the
+// StepParams'. Passed by value as a kernel argument.
+constexpr int kMaxChunks = 32;
+struct FwdChunks {
+  int32_t n;
+  const void* k[kMaxChunks];
+  const void* v[kMaxChunks];
+  SegMap km[kMaxChunks];
+};
+
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_step_fwd(const StepParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_step_bwd(const StepParams& p, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_fwd_chunks(const StepParams& p, const FwdChunks& ch, int head_dim,
+                             hipStream_t s);
 hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, int64_t row_begin,
                             int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,
                             const float* lse_step, hipStream_t s);

@@ -8,7 +8,8 @@ and Causal Imbalance of Ring Attention"; "3. Double-Ring Asynchronous
 Communication Pipeline"). Forward: the first step writes the running (O, LSE)
 directly; every later step is folded into it, either by the fused
 ring_attn_step_fwd_merge (default) or by ring_attn_step_fwd then lse_merge
-(merge="separate", over the rows the step gave any visible key). Backward:
+(merge="separate", over the rows the step gave any visible key); merge="chunks"
+runs all steps in one ring_attn_fwd_chunks launch (bf16). Backward:
 ra_bwd_delta (D = rowsum(dO O) and O in bf16), dq cleared with ra_fill_f32,
 then ring_attn_step_bwd per step with the final LSE.
 
@@ -61,8 +62,10 @@ class ShareRing(_Timed):
     def __init__(self, S, inner, outer, rank, hq, hkv, d, dtype="bf16", scale=None,
                  device="cuda", causal=1, merge="fused", layout="zigzag", kv_rings="one",
                  buffers=None):
-        if merge not in ("fused", "separate"):
-            raise ValueError(f"merge must be 'fused' or 'separate', not {merge!r}")
+        if merge not in ("fused", "separate", "chunks"):
+            raise ValueError(f"merge must be 'fused', 'separate' or 'chunks', not {merge!r}")
+        if merge == "chunks" and dtype != "bf16":
+            raise ValueError("merge='chunks' (all steps in one launch) runs the bf16 kernels only")
         if layout not in ("zigzag", "contiguous"):
             raise ValueError(f"layout must be 'zigzag' or 'contiguous', not {layout!r}")
         if kv_rings not in ("one", "ab") or (kv_rings == "ab" and layout != "zigzag"):
@@ -154,6 +157,13 @@ class ShareRing(_Timed):
 
     def forward(self, q, K, V, stream=None):
         """Running (O fp32 [L][hq][d], LSE fp32 [hq][L]) after all P steps."""
+        if self.merge == "chunks":
+            ks = [self._kv(K, j, off) for j, off, _ in self.launches]
+            vs = [self._kv(V, j, off) for j, off, _ in self.launches]
+            with self._t("step_fwd"):
+                B.ring_attn_fwd_chunks([d for _, _, d in self.launches], q, ks, vs, self.o_acc,
+                                       self.lse_acc, stream)
+            return self.o_acc, self.lse_acc
         for t, (j, off, desc) in enumerate(self.launches):
             k, v = self._kv(K, j, off), self._kv(V, j, off)
             if t == 0:

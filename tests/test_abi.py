@@ -230,3 +230,32 @@ def test_ring_merge_rows_are_the_rows_that_see_a_key(layout, S, inner, outer, r,
         want = np.zeros(len(pos_q), bool)
         want[r0:r0 + cnt] = True
         assert np.array_equal(sees, want), (j, off)
+
+
+def test_fwd_chunks_rejects_before_device_work():
+    """The one-launch forward of all ring steps: argument errors come back as
+    status codes with no device work."""
+    g = good_desc()
+
+    def call(descs, ks=None, vs=None, q=16, o=16, lse=16):
+        n = len(descs)
+        ks = [16] * n if ks is None else ks
+        vs = [16] * n if vs is None else vs
+        with pytest.raises(B.RaError) as e:
+            B.ring_attn_fwd_chunks(descs, q, ks, vs, o, lse, stream=0)
+        return e.value.status
+
+    assert call([]) == B.RA_EINVAL                                   # no chunk
+    assert call([g] * 33) == B.RA_EUNSUPPORTED                       # more than 32 chunks
+    assert call([g, good_desc(hq=4)]) == B.RA_EINVAL                 # query side differs
+    assert call([g, good_desc(q_segments=((64, 448), 64))]) == B.RA_EINVAL
+    assert call([g, good_desc(k_strides=(384, 128))]) == B.RA_EINVAL  # K strides differ
+    assert call([g, good_desc(head_dim=96)]) == B.RA_EUNSUPPORTED    # invalid chunk
+    f32 = dict(dtype=B.RA_F32)
+    assert call([good_desc(**f32), good_desc(**f32)]) == B.RA_EUNSUPPORTED  # bf16 only
+    assert call([g], q=0) == B.RA_EINVAL                             # null q
+    assert call([g], o=8) == B.RA_EALIGN                             # misaligned o
+    assert call([g, g], ks=[16, 0]) == B.RA_EINVAL                   # null K of a chunk
+    assert call([g, g], vs=[16, 24]) == B.RA_EALIGN                  # misaligned V of a chunk
+    with pytest.raises(ValueError):
+        B.ring_attn_fwd_chunks([g, g], 16, [16], [16, 16], 16, 16, stream=0)
