@@ -340,9 +340,11 @@ def main():
     # algorithmic flops per launch: each ring step carries 1/P of the share's pairs
     # (2b^2 per head per step, +b on the diagonal step); averaged over the P launches
     n_launch = len(ring.launches)   # P, or 2P with the block A / block B rings
-    bwd_launch_flops = bwd_flops / n_launch
+    # with --merge chunks the backward is one call over all steps
+    chunks = args.merge == "chunks"
+    bwd_launch_flops = bwd_flops if chunks else bwd_flops / n_launch
     # with --merge chunks the forward is one launch over all steps
-    fwd_launch_flops = fwd_flops if args.merge == "chunks" else fwd_flops / n_launch
+    fwd_launch_flops = fwd_flops if chunks else fwd_flops / n_launch
     bwd_tflops = bwd_launch_flops / (bwd_ms * 1e-3) / 1e12
     fwd_tflops = fwd_launch_flops / (fwd_ms * 1e-3) / 1e12
     merge_bytes = merge_rows * cfg.hq * (cfg.d * 4 * 3 + 4 * 3)
@@ -375,12 +377,16 @@ def main():
         "step_fwd_tflops": round(fwd_tflops, 1),
         "lse_merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms else None,
         "bwd_delta_gbs": round(delta_bytes / (delta_ms * 1e-3) / 1e9, 1) if delta_ms else None,
-        "roofline": {"bound": "mfma", "kernel": "ring_attn_step_bwd", "achieved": round(bwd_tflops, 1),
+        # with --merge chunks the dominant call is ring_attn_bwd_chunks (its dQ
+        # launch and one dK/dV launch per chunk); the recorded counters are the
+        # per-step kernels', so they are not quoted for it
+        "roofline": {"bound": "mfma", "kernel": "ring_attn_bwd_chunks" if chunks else "ring_attn_step_bwd",
+                     "achieved": round(bwd_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(cfg.name)},
+                     "traffic": None if chunks else recorded_traffic(cfg.name)},
     }
-    util = recorded_mfma_util(cfg.name)
+    util = None if chunks else recorded_mfma_util(cfg.name)
     if util is not None:
         out["mfma_busy_pct"] = util
     if wrapped:

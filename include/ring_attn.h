@@ -142,6 +142,26 @@ ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void*
                                float* lse, ra_stream_t stream);
 
 /*
+ * ring_attn_bwd_chunks -- the backward of all n ring steps: dQ of every chunk
+ * in one launch, summed in registers over the chunks and written once (no
+ * read-modify-write of dQ per step), then dK/dV of each chunk as
+ * ring_attn_step_bwd computes them. Same arithmetic as ring_attn_step_bwd over
+ * the chunks (dQ's summation order over chunks differs from accumulating it
+ * step by step); for a GPU that holds every chunk, like ring_attn_fwd_chunks.
+ * descs: n descriptors (chunk i's key side and dkv_accumulate in descs[i]; all
+ * other fields, including the dout and dK strides, equal to descs[0]'s).
+ * k, v, dk, dv: host arrays of n device pointers (chunk i's K, V and its dK,
+ * dV outputs, fp32 with the dk strides; added to when dkv_accumulate).
+ * dq: fp32 with descs[0]'s o strides, WRITTEN (not accumulated). lse, delta:
+ * the final LSE and D, fp32 [hq][lq]. 1 <= n <= 32; bf16 only. Errors as for
+ * ring_attn_fwd_chunks and ring_attn_step_bwd.
+ */
+ra_status ring_attn_bwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,
+                               const void* const* k, const void* const* v, const void* dout,
+                               const float* lse, const float* delta, float* dq,
+                               float* const* dk, float* const* dv, ra_stream_t stream);
+
+/*
  * ring_attn_step_bwd -- one step's share of the attention gradient, driven by
  * the FINAL log-sum-exp and D of the rows (saved-LSE recompute).
  *

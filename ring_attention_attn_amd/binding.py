@@ -18,7 +18,7 @@ RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EALIGN, RA_EDEVICE = 0, 1, 2, 3, 4
 RA_BF16, RA_F32 = 0, 1
 
 EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_fwd_merge", "ring_attn_fwd_chunks",
-           "ring_attn_step_bwd", "lse_merge",
+           "ring_attn_step_bwd", "ring_attn_bwd_chunks", "lse_merge",
            "ra_bwd_delta",
            "head_permute", "ra_fill_f32", "ra_zigzag_positions", "ra_zigzag_segments",
            "ra_double_ring_order", "ra_validate_step", "ra_status_str")
@@ -66,6 +66,7 @@ def lib():
             "ring_attn_step_fwd": [pd, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_fwd_merge": [pd, vp, vp, vp, vp, vp, vp],
             "ring_attn_fwd_chunks": [pd, i32, vp, vp, vp, vp, vp, vp],
+            "ring_attn_bwd_chunks": [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "ring_attn_step_bwd": [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "lse_merge": [i64, i32, i32, i64, i64, vp, vp, vp, vp, vp],
             "ra_bwd_delta": [i64, i32, i32, i32, vp, vp, vp, vp, vp],
@@ -191,6 +192,23 @@ def ring_attn_fwd_chunks(descs, q, ks, vs, o, lse, stream=None):
     vp_ = (ctypes.c_void_p * max(n, 1))(*[_ptr(v) for v in vs])
     _check(lib().ring_attn_fwd_chunks(arr, n, _ptr(q), kp, vp_, _ptr(o), _ptr(lse),
                                       _stream(stream)), "ring_attn_fwd_chunks")
+
+
+def ring_attn_bwd_chunks(descs, q, ks, vs, dout, lse, delta, dq, dks, dvs, stream=None):
+    """All ring steps of the backward: descs, ks, vs, dks, dvs are sequences
+    (chunk i's descriptor, K, V, dK, dV); dq is written."""
+    n = len(descs)
+    if not (len(ks) == len(vs) == len(dks) == len(dvs) == n):
+        raise ValueError("ring_attn_bwd_chunks: descs, ks, vs, dks and dvs must have the same length")
+    arr = (RaStepDesc * max(n, 1))(*descs)
+    for d, k, v, dk, dv in zip(descs, ks, vs, dks, dvs):
+        _step_args(d, 1, q, k, v, dq, lse, dout, delta, dk, dv)
+
+    def parr(xs):
+        return (ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in xs])
+    _check(lib().ring_attn_bwd_chunks(arr, n, _ptr(q), parr(ks), parr(vs), _ptr(dout), _ptr(lse),
+                                      _ptr(delta), _ptr(dq), parr(dks), parr(dvs),
+                                      _stream(stream)), "ring_attn_bwd_chunks")
 
 
 def ring_attn_step_bwd(desc, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, stream=None):

@@ -173,7 +173,7 @@ ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void*
   if (lq == 0) return RA_OK;
   if (!q || !o || !lse) return RA_EINVAL;
   if (!aligned16(q) || !aligned16(o) || !aligned16(lse)) return RA_EALIGN;
-  FwdChunks ch;
+  ChunkSet ch;
   memset(&ch, 0, sizeof(ch));
   for (int i = 0; i < n; ++i) {
     const ra_step_desc* d = &descs[i];
@@ -188,6 +188,53 @@ ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void*
   StepParams p = make_params(d0);
   p.q = q; p.o = o; p.lse_out = lse;
   return from_hip(launch_fwd_chunks(p, ch, d0->head_dim, (hipStream_t)stream));
+}
+
+ra_status ring_attn_bwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,
+                               const void* const* k, const void* const* v, const void* dout,
+                               const float* lse, const float* delta, float* dq, float* const* dk,
+                               float* const* dv, ra_stream_t stream) {
+  if (!descs || n < 1 || !k || !v || !dk || !dv) return RA_EINVAL;
+  if (n > kMaxChunks) return RA_EUNSUPPORTED;
+  for (int i = 0; i < n; ++i) {
+    const ra_status st = ra_validate_step(&descs[i], 1);
+    if (st != RA_OK) return st;
+    const ra_step_desc* d = &descs[i];
+    if (!same_query_side(&descs[0], d) || d->do_ss != descs[0].do_ss ||
+        d->do_hs != descs[0].do_hs || d->dk_ss != descs[0].dk_ss || d->dk_hs != descs[0].dk_hs)
+      return RA_EINVAL;
+  }
+  const ra_step_desc* d0 = &descs[0];
+  if (d0->dtype != RA_BF16) return RA_EUNSUPPORTED;  // the MFMA kernels only
+  const int64_t lq = (int64_t)d0->q_nseg * d0->q_seg_len;
+  if (lq > 0) {
+    if (!q || !dout || !lse || !delta || !dq) return RA_EINVAL;
+    if (!aligned16(q) || !aligned16(dout) || !aligned16(lse) || !aligned16(delta) ||
+        !aligned16(dq))
+      return RA_EALIGN;
+  }
+  ChunkSet ch;
+  memset(&ch, 0, sizeof(ch));
+  float* dks[kMaxChunks];
+  float* dvs[kMaxChunks];
+  int32_t acc[kMaxChunks];
+  for (int i = 0; i < n; ++i) {
+    const ra_step_desc* d = &descs[i];
+    if ((int64_t)d->k_nseg * d->k_seg_len == 0) continue;  // an empty chunk adds nothing
+    if (!k[i] || !v[i] || !dk[i] || !dv[i]) return RA_EINVAL;
+    if (!aligned16(k[i]) || !aligned16(v[i]) || !aligned16(dk[i]) || !aligned16(dv[i]))
+      return RA_EALIGN;
+    ch.k[ch.n] = k[i];
+    ch.v[ch.n] = v[i];
+    ch.km[ch.n] = make_map(d->k_nseg, d->k_seg_len, d->k_seg_pos);
+    dks[ch.n] = dk[i];
+    dvs[ch.n] = dv[i];
+    acc[ch.n] = d->dkv_accumulate;
+    ++ch.n;
+  }
+  StepParams p = make_params(d0);
+  p.q = q; p.dout = dout; p.lse_in = lse; p.delta = delta; p.o = dq;
+  return from_hip(launch_bwd_chunks(p, ch, dks, dvs, acc, d0->head_dim, (hipStream_t)stream));
 }
 
 ra_status ring_attn_step_bwd(const ra_step_desc* d, const void* q, const void* k, const void* v,

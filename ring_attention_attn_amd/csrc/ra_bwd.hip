@@ -188,9 +188,11 @@ __global__ __launch_bounds__(64) void bwd_dkv_simple_kernel(StepParams p) {
 //     the row-major K tile. Both tiles use the XOR-swizzled layout, so the
 //     16-byte row reads and the transposing reads are free of bank conflicts.
 //     dq_acc is read-modify-written once per row at the end: no atomics.
-template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, int n_qt,
-                                                        int rows_per_wg) {
+//     MULTI: every chunk of ch in turn (K, V and key map per chunk), dQ summed
+//     in registers over the chunks and written (not accumulated) at the end.
+template <int D, bool MULTI>
+__device__ __forceinline__ void bwd_dq_body(const StepParams& p, int hpw, int n_qt,
+                                            int rows_per_wg, const ChunkSet* ch) {
   constexpr int NW = 8;
   constexpr int KT = 64;
   constexpr int TB = KT * D;     // elements per K / V tile
@@ -214,7 +216,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   const int qt = n_qt - 1 - (logical % n_qt);
   const int g = gh / nsub, hs = gh % nsub;
   const int h = g * p.group + hs * hpw + (wave % hpw);
-  const int64_t lq = p.qm.len, lk = p.km.len;
+  const int64_t lq = p.qm.len;
+  SegMap km = MULTI ? ch->km[0] : p.km;  // key map of the chunk being processed
+  int64_t lk = km.len;
   const int64_t wg_r0 = (int64_t)qt * rows_per_wg;
   const int64_t row0 = wg_r0 + (int64_t)(wave / hpw) * 32;
 
@@ -223,8 +227,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   if (wave_active) seg_bounds(p.qm, row0, row0 + 32 < lq ? row0 + 32 : lq, wq_lo, wq_hi);
   seg_bounds(p.qm, wg_r0, wg_r0 + rows_per_wg < lq ? wg_r0 + rows_per_wg : lq, gq_lo, gq_hi);
 
-  const bf16_t* K = (const bf16_t*)p.k + (int64_t)g * p.k_hs;
-  const bf16_t* V = (const bf16_t*)p.v + (int64_t)g * p.v_hs;
+  const bf16_t* K = (const bf16_t*)(MULTI ? ch->k[0] : p.k) + (int64_t)g * p.k_hs;
+  const bf16_t* V = (const bf16_t*)(MULTI ? ch->v[0] : p.v) + (int64_t)g * p.v_hs;
 
   // stale LDS must hold finite values (0 * NaN would poison dQ)
   for (int i = tid; i < TB / 8; i += NW * 64) {
@@ -260,9 +264,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
 #pragma unroll
   for (int db = 0; db < ND; ++db) qacc[db] = f32x16{};
 
-  const KeyTiles<KT> kt_wg(p.km, p.causal, gq_lo, gq_hi);
-  const KeyTiles<KT> kt_w(p.km, p.causal, wq_lo, wq_hi);
-  const int n_kt = kt_wg.n;
+  KeyTiles<KT> kt_wg(km, p.causal, gq_lo, gq_hi);
+  KeyTiles<KT> kt_w(km, p.causal, wq_lo, wq_hi);
+  int n_kt = kt_wg.n;
 
   DmaSwz<KT, D, NW, 1> kst, vst;
   kst.init(p.k_ss, wave, lane);
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!kt_w.mask_free(t)) {  // wave-uniform: one branch around branch-free code
-      const TileRows tk(p.km, (int64_t)t * KT, KT);
+      const TileRows tk(km, (int64_t)t * KT, KT);
       const MaskBounds mb(tk, qlim, 8 * hi, p.causal);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -363,23 +367,37 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   __syncthreads();  // zero-fill done before any DMA lands
-  int t = kt_wg.next(0);
-  if (t < n_kt) stage(t, B0{});
-  // tiles alternate between two buffers; unrolled so each is a distinct array
-  while (t < n_kt) {
-    wait_vmem();
-    __syncthreads();  // tile t visible in buffer 0; every wave is done with buffer 1
-    int tn = kt_wg.next(t + 1);
-    if (tn < n_kt) stage(tn, B1{});
-    compute(t, B0{});
-    t = tn;
-    if (t >= n_kt) break;
-    wait_vmem();
-    __syncthreads();
-    tn = kt_wg.next(t + 1);
-    if (tn < n_kt) stage(tn, B0{});
-    compute(t, B1{});
-    t = tn;
+  const int n_chunks = MULTI ? ch->n : 1;
+  for (int c = 0; c < n_chunks; ++c) {
+    if (MULTI && c > 0) {
+      km = ch->km[c];
+      lk = km.len;
+      K = (const bf16_t*)ch->k[c] + (int64_t)g * p.k_hs;
+      V = (const bf16_t*)ch->v[c] + (int64_t)g * p.v_hs;
+      kt_wg = KeyTiles<KT>(km, p.causal, gq_lo, gq_hi);
+      kt_w = KeyTiles<KT>(km, p.causal, wq_lo, wq_hi);
+      n_kt = kt_wg.n;
+      wait_vmem();
+      __syncthreads();  // every wave is done with the previous chunk's buffers
+    }
+    int t = kt_wg.next(0);
+    if (t < n_kt) stage(t, B0{});
+    // tiles alternate between two buffers; unrolled so each is a distinct array
+    while (t < n_kt) {
+      wait_vmem();
+      __syncthreads();  // tile t visible in buffer 0; every wave is done with buffer 1
+      int tn = kt_wg.next(t + 1);
+      if (tn < n_kt) stage(tn, B1{});
+      compute(t, B0{});
+      t = tn;
+      if (t >= n_kt) break;
+      wait_vmem();
+      __syncthreads();
+      tn = kt_wg.next(t + 1);
+      if (tn < n_kt) stage(tn, B0{});
+      compute(t, B1{});
+      t = tn;
+    }
   }
 
   if (!qok) return;
@@ -389,11 +407,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4* ptr = (f32x4*)(dq + 32 * db + 8 * i + 4 * hi);
-      f32x4 v4 = *ptr;
+      f32x4 v4 = MULTI ? f32x4{} : *ptr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) v4[j] += qacc[db][4 * i + j] * p.scale;
       *ptr = v4;
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(StepParams p, int hpw, int n_qt,
+                                                        int rows_per_wg) {
+  bwd_dq_body<D, false>(p, hpw, n_qt, rows_per_wg, nullptr);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dq_chunks_kernel(StepParams p, int hpw, int n_qt,
+                                                               int rows_per_wg, ChunkSet ch) {
+  bwd_dq_body<D, true>(p, hpw, n_qt, rows_per_wg, &ch);
 }
 
 // (2) dK, dV, key-stationary, symmetric wave pairs: a workgroup of 8 waves
@@ -732,7 +762,41 @@ hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_chunks(const StepParams& p, const ChunkSet& ch, float* const* dk,
+                         float* const* dv, const int32_t* acc, hipStream_t s) {
+  if (p.qm.len > 0) {
+    const int hpw = gcd_int(p.group, 4);
+    const int rows_per_wg = (8 / hpw) * 32;
+    const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
+    const int64_t grid = (int64_t)p.hkv * (p.group / hpw) * n_qt;
+    hipLaunchKernelGGL((bwd_dq_chunks_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw,
+                       n_qt, rows_per_wg, ch);
+  }
+  for (int c = 0; c < ch.n; ++c) {
+    StepParams pc = p;
+    pc.k = ch.k[c];
+    pc.v = ch.v[c];
+    pc.km = ch.km[c];
+    pc.dk = dk[c];
+    pc.dv = dv[c];
+    pc.dkv_accumulate = acc[c];
+    const int n_kt = (int)((pc.km.len + 127) / 128);
+    const int64_t grid = (int64_t)pc.hkv * n_kt;
+    if (grid > 0)
+      hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, pc, n_kt);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_chunks(const StepParams& p, const ChunkSet& ch, float* const* dk,
+                             float* const* dv, const int32_t* dkv_accumulate, int head_dim,
+                             hipStream_t s) {
+  return head_dim == 128 ? launch_chunks<128>(p, ch, dk, dv, dkv_accumulate, s)
+                         : launch_chunks<64>(p, ch, dk, dv, dkv_accumulate, s);
+}
 
 hipError_t launch_step_bwd(const StepParams& p, int dtype, int head_dim, hipStream_t s) {
   if (dtype == RA_BF16) return head_dim == 128 ? launch_mfma<128>(p, s) : launch_mfma<64>(p, s);

@@ -188,7 +188,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 // carried in registers from one chunk to the next and written once at the end.
 template <int D, bool MERGE, bool MULTI>
 __device__ __forceinline__ void fwd_mfma_body(const StepParams& p, int hpw, int n_qt,
-                                              int rows_per_wg, const FwdChunks* ch) {
+                                              int rows_per_wg, const ChunkSet* ch) {
   constexpr int NW = 8;            // waves per workgroup
   constexpr int KT = 64;           // keys per LDS tile
   constexpr int TB = KT * D;       // elements per K / V tile (XOR-swizzled rows, no padding)
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(StepParams p, int hpw,
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void fwd_chunks_kernel(StepParams p, int hpw, int n_qt,
-                                                            int rows_per_wg, FwdChunks ch) {
+                                                            int rows_per_wg, ChunkSet ch) {
   fwd_mfma_body<D, false, true>(p, hpw, n_qt, rows_per_wg, &ch);
 }
 
@@ -556,7 +556,7 @@ hipError_t launch_mfma(const StepParams& p, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_chunks(const StepParams& p, const FwdChunks& ch, hipStream_t s) {
+hipError_t launch_chunks(const StepParams& p, const ChunkSet& ch, hipStream_t s) {
   const int hpw = gcd_int(p.group, 4);
   const int rows_per_wg = (8 / hpw) * 32;
   const int n_qt = (int)((p.qm.len + rows_per_wg - 1) / rows_per_wg);
@@ -580,7 +580,7 @@ hipError_t launch_simple(const StepParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd_chunks(const StepParams& p, const FwdChunks& ch, int head_dim,
+hipError_t launch_fwd_chunks(const StepParams& p, const ChunkSet& ch, int head_dim,
                              hipStream_t s) {
   return head_dim == 128 ? launch_chunks<128>(p, ch, s) : launch_chunks<64>(p, ch, s);
 }

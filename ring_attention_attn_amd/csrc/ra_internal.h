@@ -58,11 +58,11 @@ struct StepParams {
   float scale_log2;        // scale * log2(e)
 };
 
-// The key-side inputs of every ring step, for the forward that runs the whole
+// The key-side inputs of every ring step, for the calls that run the whole
 // ring in one launch (bf16 only); the query side and the strides are the
 // StepParams'. Passed by value as a kernel argument.
 constexpr int kMaxChunks = 32;
-struct FwdChunks {
+struct ChunkSet {
   int32_t n;
   const void* k[kMaxChunks];
   const void* v[kMaxChunks];
@@ -72,7 +72,12 @@ struct FwdChunks {
 // kernel launchers (return hipSuccess or the launch error)
 hipError_t launch_step_fwd(const StepParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_step_bwd(const StepParams& p, int dtype, int head_dim, hipStream_t s);
-hipError_t launch_fwd_chunks(const StepParams& p, const FwdChunks& ch, int head_dim,
+hipError_t launch_fwd_chunks(const StepParams& p, const ChunkSet& ch, int head_dim,
+                             hipStream_t s);
+// dQ of all chunks in one launch (written), then dK/dV of each chunk (p's
+// dk/dv strides and dkv_accumulate; dk[i], dv[i] chunk i's outputs)
+hipError_t launch_bwd_chunks(const StepParams& p, const ChunkSet& ch, float* const* dk,
+                             float* const* dv, const int32_t* dkv_accumulate, int head_dim,
                              hipStream_t s);
 hipError_t launch_lse_merge(int64_t rows, int32_t hq, int32_t d, int64_t row_begin,
                             int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,

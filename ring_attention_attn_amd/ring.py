@@ -9,7 +9,8 @@ Communication Pipeline"). Forward: the first step writes the running (O, LSE)
 directly; every later step is folded into it, either by the fused
 ring_attn_step_fwd_merge (default) or by ring_attn_step_fwd then lse_merge
 (merge="separate", over the rows the step gave any visible key); merge="chunks"
-runs all steps in one ring_attn_fwd_chunks launch (bf16). Backward:
+runs all steps in one ring_attn_fwd_chunks launch and the backward as one
+ring_attn_bwd_chunks call (bf16). Backward:
 ra_bwd_delta (D = rowsum(dO O) and O in bf16), dq cleared with ra_fill_f32,
 then ring_attn_step_bwd per step with the final LSE.
 
@@ -187,6 +188,14 @@ class ShareRing(_Timed):
         with self._t("bwd_delta"):
             B.ra_bwd_delta(self.L, self.hq, self.d, _RA_DTYPE[self.dtype], self.o_acc, dout,
                            self.delta, self.o_lowp if self.dtype == "bf16" else None, stream)
+        if self.merge == "chunks":
+            L = self.launches
+            with self._t("step_bwd"):
+                B.ring_attn_bwd_chunks([d for _, _, d in L], q, [self._kv(K, j, o) for j, o, _ in L],
+                                       [self._kv(V, j, o) for j, o, _ in L], dout, self.lse_acc,
+                                       self.delta, self.dq, [self._kv(self.dk, j, o) for j, o, _ in L],
+                                       [self._kv(self.dv, j, o) for j, o, _ in L], stream)
+            return self.dq, self.dk, self.dv
         with self._t("fill"):
             B.ra_fill_f32(self.dq, self.dq.numel(), 0.0, stream)
         for j, off, desc in self.launches:

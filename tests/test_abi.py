@@ -259,3 +259,32 @@ def test_fwd_chunks_rejects_before_device_work():
     assert call([g, g], vs=[16, 24]) == B.RA_EALIGN                  # misaligned V of a chunk
     with pytest.raises(ValueError):
         B.ring_attn_fwd_chunks([g, g], 16, [16], [16, 16], 16, 16, stream=0)
+
+
+def test_bwd_chunks_rejects_before_device_work():
+    """The backward of all ring steps in one call: argument errors come back as
+    status codes with no device work."""
+    g = good_desc()
+
+    def call(descs, ks=None, vs=None, dks=None, dvs=None, q=16, dout=16, dq=16):
+        n = len(descs)
+        f = lambda x: [16] * n if x is None else x
+        with pytest.raises(B.RaError) as e:
+            B.ring_attn_bwd_chunks(descs, q, f(ks), f(vs), dout, 16, 16, dq, f(dks), f(dvs),
+                                   stream=0)
+        return e.value.status
+
+    assert call([]) == B.RA_EINVAL
+    assert call([g] * 33) == B.RA_EUNSUPPORTED
+    assert call([g, good_desc(hkv=4)]) == B.RA_EINVAL                 # query side differs
+    assert call([g, good_desc(do_strides=(2048, 128))]) == B.RA_EINVAL  # dout strides differ
+    assert call([g, good_desc(dk_strides=(384, 128))]) == B.RA_EINVAL   # dK strides differ
+    f32 = dict(dtype=B.RA_F32)
+    assert call([good_desc(**f32)]) == B.RA_EUNSUPPORTED               # bf16 only
+    assert call([g], dout=0) == B.RA_EINVAL
+    assert call([g], dq=8) == B.RA_EALIGN
+    assert call([g, g], dks=[16, 0]) == B.RA_EINVAL                    # null dK of a chunk
+    assert call([g, g], dvs=[16, 40]) == B.RA_EALIGN
+    with pytest.raises(ValueError):
+        B.ring_attn_bwd_chunks([g, g], 16, [16, 16], [16, 16], 16, 16, 16, 16, [16], [16, 16],
+                               stream=0)

@@ -94,11 +94,12 @@ def test_share_separate_merge_matches_fused(case):
 
 
 @pytest.mark.parametrize("case", [c for c in SHARE_CASES if c[8] == "bf16"], ids=lambda c: c[0])
-def test_share_chunks_forward_matches_oracle(case):
+def test_share_chunks_matches_oracle(case):
     """The forward of all steps in one launch (running max, sum and output kept
-    in registers across chunks) against the oracle, and close to the per-step
-    fused path (the same softmax; only the rounding of the intermediate
-    normalisation differs). The backward then runs from its O and LSE."""
+    in registers across chunks) and the backward of all steps in one call (dQ
+    summed in registers over the chunks and written once) against the oracle,
+    and close to the per-step path (the same arithmetic; only the rounding of
+    the intermediate normalisation and dQ's summation order differ)."""
     name, S, inner, outer, r, hq, hkv, d, dtype = case
     P = inner * outer
     x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=3000 + S + r)
@@ -118,6 +119,8 @@ def test_share_chunks_forward_matches_oracle(case):
     assert np.array_equal(np.isneginf(fused["LSE"]), np.isneginf(got["LSE"]))
     assert max_abs(fused["O"], got["O"]) < 1e-2
     assert max_abs(fused["LSE"][fin], got["LSE"][fin]) < 1e-4
+    for t in ("dQ", "dK", "dV"):
+        assert max_abs(fused[t], got[t]) < 1e-2, t
 
 
 @pytest.mark.parametrize("r", [0, 1, 3])
