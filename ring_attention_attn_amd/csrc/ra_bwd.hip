@@ -13,6 +13,7 @@
 // key-stationary), deterministic.
 #include <limits.h>
 #include <math.h>
+#include <string.h>
 
 #include <type_traits>
 
@@ -438,8 +439,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_chunks_kernel(StepParams p, int
 //      registers and its partner's from LDS. Q and dO tiles reach LDS by DMA
 //      one step ahead (two buffers each, XOR-swizzled), with the tile's LSE
 //      (log2 units) and D. Every dK/dV element has one writer.
+//      The workgroup's KV head g and key block kt come from its caller.
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
+__device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, const int kt) {
   constexpr int NW = 8;
   constexpr int KB = 128;      // keys per workgroup
   constexpr int QT = 64;       // query rows per tile
@@ -463,9 +465,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
   const int l32 = lane & 31, hi = lane >> 5;
   const int srow = sigma32(l32);
 
-  const int logical = xcd_remap(blockIdx.x, p.hkv * n_kt, p.hkv);
-  const int g = logical / n_kt;
-  const int kt = logical % n_kt;
   const int64_t lq = p.qm.len, lk = p.km.len;
   const int64_t key0 = (int64_t)kt * KB;
   const int64_t key1 = key0 + KB < lk ? key0 + KB : lk;
@@ -724,6 +723,46 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt)
     }
 }
 
+// one ring step: workgroups in KV-head-major order, spread so that each XCD
+// runs the key blocks of as few KV heads as possible (they share Q / dO)
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(StepParams p, int n_kt) {
+  const int logical = xcd_remap(blockIdx.x, p.hkv * n_kt, p.hkv);
+  bwd_dkv_body<D>(p, logical / n_kt, logical % n_kt);
+}
+
+// The dK/dV outputs of every chunk of a ChunkSet, for one launch over all of
+// them; kt0[c] is the first key block of chunk c in a KV head's sequence of
+// blocks (kt0[n] = blocks per KV head).
+struct DkvChunks {
+  int32_t n;
+  int32_t kt0[kMaxChunks + 1];
+  float* dk[kMaxChunks];
+  float* dv[kMaxChunks];
+  int32_t acc[kMaxChunks];
+};
+
+// all chunks: per KV head, the key blocks of chunk 0, then chunk 1, ...; the
+// same XCD spread as one step's launch, over the longer sequence
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_chunks_kernel(StepParams p, ChunkSet ch,
+                                                                DkvChunks dc) {
+  const int per_g = dc.kt0[dc.n];
+  const int logical = xcd_remap(blockIdx.x, p.hkv * per_g, p.hkv);
+  const int g = logical / per_g;
+  const int r = logical % per_g;
+  int c = 0;
+  while (c + 1 < dc.n && r >= dc.kt0[c + 1]) ++c;
+  StepParams pc = p;
+  pc.k = ch.k[c];
+  pc.v = ch.v[c];
+  pc.km = ch.km[c];
+  pc.dk = dc.dk[c];
+  pc.dv = dc.dv[c];
+  pc.dkv_accumulate = dc.acc[c];
+  bwd_dkv_body<D>(pc, g, r - dc.kt0[c]);
+}
+
 int gcd_int(int a, int b) {
   while (b) {
     int t = a % b;
@@ -773,19 +812,25 @@ hipError_t launch_chunks(const StepParams& p, const ChunkSet& ch, float* const* 
     hipLaunchKernelGGL((bwd_dq_chunks_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, hpw,
                        n_qt, rows_per_wg, ch);
   }
+  static_assert(sizeof(StepParams) + sizeof(ChunkSet) + sizeof(DkvChunks) <= 4096,
+                "kernel arguments above 4 KiB");
+  DkvChunks dc;
+  memset(&dc, 0, sizeof(dc));
+  dc.n = ch.n;
+  int64_t per_g = 0;
   for (int c = 0; c < ch.n; ++c) {
-    StepParams pc = p;
-    pc.k = ch.k[c];
-    pc.v = ch.v[c];
-    pc.km = ch.km[c];
-    pc.dk = dk[c];
-    pc.dv = dv[c];
-    pc.dkv_accumulate = acc[c];
-    const int n_kt = (int)((pc.km.len + 127) / 128);
-    const int64_t grid = (int64_t)pc.hkv * n_kt;
-    if (grid > 0)
-      hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, pc, n_kt);
+    dc.kt0[c] = (int32_t)per_g;
+    per_g += (ch.km[c].len + 127) / 128;
+    dc.dk[c] = dk[c];
+    dc.dv[c] = dv[c];
+    dc.acc[c] = acc[c];
   }
+  dc.kt0[ch.n] = (int32_t)per_g;
+  const int64_t grid = (int64_t)p.hkv * per_g;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (grid > 0)
+    hipLaunchKernelGGL((bwd_dkv_chunks_kernel<D>), dim3((unsigned)grid), dim3(512), 0, s, p, ch,
+                       dc);
   return hipGetLastError();
 }
 

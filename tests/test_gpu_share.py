@@ -178,6 +178,34 @@ def test_ab_rings_share(case):
     assert max_abs(dk.cpu().numpy(), one["dK"]) < 2e-3
 
 
+@pytest.mark.parametrize("case", [c for c in SHARE_CASES if c[8] == "bf16"], ids=lambda c: c[0])
+def test_bwd_chunks_matches_per_step(case):
+    """ring_attn_bwd_chunks from the same forward (O, LSE, D) as the per-step
+    backward: dK and dV come from the same key-block computation (bit for bit,
+    whatever the outputs held before, since each chunk's first visit writes);
+    dQ is written, not accumulated, and equals the per-step sum up to its
+    fp32 summation order."""
+    from ring_attention_attn_amd import binding as B
+    from ring_attention_attn_amd.ring import ShareRing
+    name, S, inner, outer, r, hq, hkv, d, dtype = case
+    x = share_inputs(S, inner * outer, r, hq, hkv, d, dtype, seed=4000 + S + r)
+    q, do = to_device(x["q"], dtype), to_device(x["do"], dtype)
+    K, V = to_device(x["k_ch"], dtype), to_device(x["v_ch"], dtype)
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype)
+    ring.forward(q, K, V)
+    dq1, dk1, dv1 = (t.clone() for t in ring.backward(q, K, V, do))
+    dq2, dk2, dv2 = (torch.full_like(t, float("nan")) for t in (dq1, dk1, dv1))
+    L = ring.launches
+    B.ring_attn_bwd_chunks([dsc for _, _, dsc in L], q, [ring._kv(K, j, o) for j, o, _ in L],
+                           [ring._kv(V, j, o) for j, o, _ in L], do, ring.lse_acc, ring.delta, dq2,
+                           [ring._kv(dk2, j, o) for j, o, _ in L],
+                           [ring._kv(dv2, j, o) for j, o, _ in L])
+    torch.cuda.synchronize()
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    assert torch.isfinite(dq2).all()
+    assert (dq1 - dq2).abs().max().item() <= 1e-5 * dq1.abs().max().item()
+
+
 def test_ring_order_invariance():
     """The merged result does not depend on the order the chunks are visited in
     (up to fp32 rounding of the merge)."""
