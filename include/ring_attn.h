@@ -54,6 +54,9 @@ typedef enum {
 
 typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
 
+/* most chunks one ring_attn_fwd_chunks / ring_attn_bwd_chunks call takes */
+#define RA_MAX_CHUNKS 32
+
 typedef void* ra_stream_t; /* a hipStream_t */
 
 /*
@@ -134,7 +137,7 @@ ra_status ring_attn_step_fwd_merge(const ra_step_desc* desc, const void* q, cons
  * must equal descs[0]'s (RA_EINVAL otherwise). k, v: host arrays of n device
  * pointers (chunk i's K and V). o: fp32 [lq][hq][d] (descs[0]'s o strides),
  * lse: fp32 [hq][lq], both written (rows with no visible key anywhere: O = 0,
- * LSE = -inf). 1 <= n <= 32 (RA_EUNSUPPORTED beyond); bf16 only
+ * LSE = -inf). 1 <= n <= RA_MAX_CHUNKS (RA_EUNSUPPORTED beyond); bf16 only
  * (RA_EUNSUPPORTED for fp32). Chunks with lk == 0 are skipped.
  */
 ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,
@@ -153,7 +156,7 @@ ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void*
  * k, v, dk, dv: host arrays of n device pointers (chunk i's K, V and its dK,
  * dV outputs, fp32 with the dk strides; added to when dkv_accumulate).
  * dq: fp32 with descs[0]'s o strides, WRITTEN (not accumulated). lse, delta:
- * the final LSE and D, fp32 [hq][lq]. 1 <= n <= 32; bf16 only. Errors as for
+ * the final LSE and D, fp32 [hq][lq]. 1 <= n <= RA_MAX_CHUNKS; bf16 only. Errors as for
  * ring_attn_fwd_chunks and ring_attn_step_bwd.
  */
 ra_status ring_attn_bwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EALIGN, RA_EDEVICE = 0, 1, 2, 3, 4
 RA_BF16, RA_F32 = 0, 1
+RA_MAX_CHUNKS = 32   # include/ring_attn.h
 
 EXPORTS = ("ring_attn_step_fwd", "ring_attn_step_fwd_merge", "ring_attn_fwd_chunks",
            "ring_attn_step_bwd", "ring_attn_bwd_chunks", "lse_merge",

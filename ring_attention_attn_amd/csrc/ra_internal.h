@@ -61,7 +61,7 @@ struct StepParams {
 // The key-side inputs of every ring step, for the calls that run the whole
 // ring in one launch (bf16 only); the query side and the strides are the
 // StepParams'. Passed by value as a kernel argument.
-constexpr int kMaxChunks = 32;
+constexpr int kMaxChunks = RA_MAX_CHUNKS;
 struct ChunkSet {
   int32_t n;
   const void* k[kMaxChunks];

@@ -136,6 +136,9 @@ class ShareRing(_Timed):
                 # own block's rows, which no other launch touches)
                 self.launches.append((j, 0, desc((k_seg[0],), kb, 0)))
                 self.launches.append((j, kb, desc((k_seg[1],), kb, 0)))
+        if merge == "chunks" and len(self.launches) > B.RA_MAX_CHUNKS:
+            raise ValueError(f"merge='chunks' takes at most {B.RA_MAX_CHUNKS} launches per call, "
+                             f"this ring has {len(self.launches)}")
 
     def _kv(self, X, j, off):
         return X[j] if off == 0 else X[j][off:]

@@ -288,3 +288,21 @@ def test_bwd_chunks_rejects_before_device_work():
     with pytest.raises(ValueError):
         B.ring_attn_bwd_chunks([g, g], 16, [16, 16], [16, 16], 16, 16, 16, 16, [16], [16, 16],
                                stream=0)
+
+
+def test_chunk_limit_constant_and_driver_check():
+    """The binding's RA_MAX_CHUNKS is the header's; the ring driver refuses a
+    chunks-mode ring with more launches than one call takes (32 chunks as
+    block A / block B rings are 64 launches), and accepts 32."""
+    from ring_attention_attn_amd.ring import ShareRing
+    m = re.search(r"#define\s+RA_MAX_CHUNKS\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == B.RA_MAX_CHUNKS
+    with pytest.raises(ValueError, match="at most 32"):
+        ShareRing(2048, 32, 1, 0, 1, 1, 64, "bf16", device="cpu", merge="chunks", kv_rings="ab")
+    ring = ShareRing(2048, 32, 1, 0, 1, 1, 64, "bf16", device="cpu", merge="chunks")
+    assert len(ring.launches) == 32
+    # a call with one descriptor more than the limit is refused before device work
+    with pytest.raises(B.RaError) as e:
+        B.ring_attn_fwd_chunks([good_desc()] * (B.RA_MAX_CHUNKS + 1), 16, [16] * 33, [16] * 33,
+                               16, 16, stream=0)
+    assert e.value.status == B.RA_EUNSUPPORTED

@@ -145,17 +145,19 @@ def test_contiguous_layout_share(r):
     assert rel_l2(got["dQ"], want["dQ"]) < 1e-2
 
 
+@pytest.mark.parametrize("merge", ["fused", "chunks"])
 @pytest.mark.parametrize("case", [SHARE_CASES[4], SHARE_CASES[7]], ids=lambda c: c[0])
-def test_ab_rings_share(case):
+def test_ab_rings_share(case, merge):
     """Each step as two launches, one per block of the KV chunk (the block A and
-    block B rings), against the oracle and the one-launch steps."""
+    block B rings), per step or all in one call, against the oracle and the
+    one-launch steps."""
     name, S, inner, outer, r, hq, hkv, d, dtype = case
     P = inner * outer
     x = share_inputs(S, P, r, hq, hkv, d, dtype, seed=4000 + S + r)
     from ring_attention_attn_amd.ring import ShareRing
     q, do = to_device(x["q"], dtype), to_device(x["do"], dtype)
     K, V = to_device(x["k_ch"], dtype), to_device(x["v_ch"], dtype)
-    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype, kv_rings="ab")
+    ring = ShareRing(S, inner, outer, r, hq, hkv, d, dtype, kv_rings="ab", merge=merge)
     assert len(ring.launches) == 2 * P
     o, lse = ring.forward(q, K, V)
     dq, dk, dv = ring.backward(q, K, V, do)
@@ -256,12 +258,12 @@ def head_parallel_inputs(S, P, r, H, Hkv, d, hp, g, seed):
     return x
 
 
-def run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x, sentinel=7.25):
+def run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x, sentinel=7.25, merge="fused"):
     """The 2D-Attention share through HeadParallelShare. Exchange slots other
     than g are filled with ``sentinel`` first: they stand for the other
     head-parallel ranks' data and must come back bit for bit."""
     from ring_attention_attn_amd.ring import HeadParallelShare
-    hp_share = HeadParallelShare(S, inner, outer, r, H, Hkv, d, hp, group=g)
+    hp_share = HeadParallelShare(S, inner, outer, r, H, Hkv, d, hp, group=g, merge=merge)
     for t in (hp_share.o_x, hp_share.dq_x, hp_share.dk_x, hp_share.dv_x):
         t.fill_(sentinel)
     dev = lambda a: to_device(a, "bf16")
@@ -292,8 +294,9 @@ def run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x, sentinel=7.25):
     return hp_share, got
 
 
+@pytest.mark.parametrize("merge", ["fused", "chunks"])
 @pytest.mark.parametrize("case", HP_CASES, ids=lambda c: c[0])
-def test_head_parallel_share_matches_oracle(case):
+def test_head_parallel_share_matches_oracle(case, merge):
     """2D-Attention: head permute of Q/dO and of the own K/V chunk, the ring on
     head group g, inverse permute of O/dQ and of the own chunk's dK/dV. Outputs
     in the all-head layout against the oracle on the full-head tensors
@@ -301,7 +304,7 @@ def test_head_parallel_share_matches_oracle(case):
     name, S, inner, outer, r, H, Hkv, d, hp, g = case
     P = inner * outer
     x = head_parallel_inputs(S, P, r, H, Hkv, d, hp, g, seed=6000 + S + r)
-    _, got = run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x)
+    _, got = run_head_parallel(S, inner, outer, r, H, Hkv, d, hp, g, x, merge=merge)
     pos = oracle.zigzag_positions(S, P, r)
     w = lambda a: widen(a, "bf16")
     want = oracle.share_backward(w(x["q"]), w(x["k_nat"]), w(x["v_nat"]), w(x["do"]), pos,
