@@ -375,6 +375,10 @@ def main():
                                     "lse_merge": round(merge_ms, 4),
                                     "bwd_delta": round(delta_ms, 4)},
         "step_fwd_tflops": round(fwd_tflops, 1),
+        "step_bwd_tflops": round(bwd_tflops, 1),
+        # the same step counted without the backward's QK^T recompute (12 d per
+        # visible pair instead of 14 d), so the headline cannot be read as inflated
+        "value_without_recompute": round(value * 12 / 14, 2),
         "lse_merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms else None,
         "bwd_delta_gbs": round(delta_bytes / (delta_ms * 1e-3) / 1e9, 1) if delta_ms else None,
         # with --merge chunks the dominant call is ring_attn_bwd_chunks (its dQ
