@@ -567,6 +567,17 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
     // instructions across it), so the LDS latency hides behind the products
     constexpr int AH = 3;
     bf16x8 qa[AH + 1], ga[AH + 1];
+    // LSE and D of row chunk cc: chunk 0's are read among the last products
+    // (after the last operand read), chunk 1's at the start of chunk 0's
+    // vector work, so neither waits on the LDS before its first use
+    f32x4 ld[2][4];
+    auto read_ld = [&](int cc) {
+      const int qo = 32 * hf + 16 * cc + 8 * hi;
+      ld[cc][0] = *(const f32x4*)(&sL[B][qo]);
+      ld[cc][1] = *(const f32x4*)(&sL[B][qo + 4]);
+      ld[cc][2] = *(const f32x4*)(&sD[B][qo]);
+      ld[cc][3] = *(const f32x4*)(&sD[B][qo + 4]);
+    };
 #pragma unroll
     for (int i = 0; i < AH; ++i) {
       qa[i] = *(const bf16x8*)(cQ + (roff ^ (32 * i)));
@@ -579,6 +590,7 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
         qa[cn % (AH + 1)] = *(const bf16x8*)(cQ + (roff ^ (32 * cn)));
         ga[cn % (AH + 1)] = *(const bf16x8*)(cG + (roff ^ (32 * cn)));
       }
+      if (c == NC - AH) read_ld(0);
       sacc = mfma32(qa[c % (AH + 1)], kreg[c], sacc);
       pacc = mfma32(ga[c % (AH + 1)], vreg[c], pacc);
       __builtin_amdgcn_sched_barrier(0);
@@ -595,14 +607,12 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
     }
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      const int qo = 32 * hf + 16 * cc + 8 * hi;
-      const f32x4 la = *(const f32x4*)(&sL[B][qo]), lb = *(const f32x4*)(&sL[B][qo + 4]);
-      const f32x4 da = *(const f32x4*)(&sD[B][qo]), db_ = *(const f32x4*)(&sD[B][qo + 4]);
+      if (cc == 0) read_ld(1);
       float pv[8], sv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float l2 = e < 4 ? la[e] : lb[e - 4];
-        const float dl = e < 4 ? da[e] : db_[e - 4];
+        const float l2 = e < 4 ? ld[cc][0][e] : ld[cc][1][e - 4];
+        const float dl = e < 4 ? ld[cc][2][e] : ld[cc][3][e - 4];
         pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * cc + e], p.scale_log2, -l2));
         sv[e] = pv[e] * (pacc[8 * cc + e] - dl);
       }
