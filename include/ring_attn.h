@@ -147,17 +147,21 @@ ra_status ring_attn_fwd_chunks(const ra_step_desc* descs, int32_t n, const void*
 /*
  * ring_attn_bwd_chunks -- the backward of all n ring steps: dQ of every chunk
  * in one launch, summed in registers over the chunks and written once (no
- * read-modify-write of dQ per step), then dK/dV of each chunk as
- * ring_attn_step_bwd computes them. Same arithmetic as ring_attn_step_bwd over
- * the chunks (dQ's summation order over chunks differs from accumulating it
- * step by step); for a GPU that holds every chunk, like ring_attn_fwd_chunks.
+ * read-modify-write of dQ per step), then dK/dV of every chunk in a second
+ * launch, each chunk's exactly as ring_attn_step_bwd computes them (bit for
+ * bit from the same LSE and D). Same arithmetic as ring_attn_step_bwd over the
+ * chunks (dQ's summation order over chunks differs from accumulating it step
+ * by step); for a GPU that holds every chunk, like ring_attn_fwd_chunks.
+ * A chunk with lk == 0 is skipped (its pointers are not read, its dK/dV left
+ * as they are); with lq == 0, dq, q, dout, lse and delta are not read and
+ * dK/dV are written as zeros (left as they are when dkv_accumulate).
  * descs: n descriptors (chunk i's key side and dkv_accumulate in descs[i]; all
  * other fields, including the dout and dK strides, equal to descs[0]'s).
  * k, v, dk, dv: host arrays of n device pointers (chunk i's K, V and its dK,
  * dV outputs, fp32 with the dk strides; added to when dkv_accumulate).
  * dq: fp32 with descs[0]'s o strides, WRITTEN (not accumulated). lse, delta:
- * the final LSE and D, fp32 [hq][lq]. 1 <= n <= RA_MAX_CHUNKS; bf16 only. Errors as for
- * ring_attn_fwd_chunks and ring_attn_step_bwd.
+ * the final LSE and D, fp32 [hq][lq]. 1 <= n <= RA_MAX_CHUNKS; bf16 only.
+ * Errors as for ring_attn_fwd_chunks and ring_attn_step_bwd.
  */
 ra_status ring_attn_bwd_chunks(const ra_step_desc* descs, int32_t n, const void* q,
                                const void* const* k, const void* const* v, const void* dout,

@@ -1,6 +1,6 @@
 """ring_attn_fwd_chunks / ring_attn_bwd_chunks at their edges: the largest
 chunk count (32), chunks of different lengths with an empty one among them,
-and no key at all. Each case runs against the fp64 oracle over the union of
+and no key or no query row at all. Each case runs against the fp64 oracle over the union of
 the chunks' keys (softmax over a union of key sets is what the ring's merges
 compute) and against the per-step entry points on the same descriptors."""
 import math
@@ -164,3 +164,25 @@ def test_chunks_without_keys():
     assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
     assert bool((dq == 0).all())
     assert all(bool((t == 3.5).all()) for t in dk + dv)
+
+
+def test_chunks_without_queries():
+    """No query row (lq = 0): the forward does nothing, the backward writes
+    every chunk's dK/dV as zeros and reads no query-side argument."""
+    S, P, r, hq, hkv, d = 1024, 4, 1, 4, 2, 128
+    descs, x, ks, vs, kpos, pos_q = chunk_set(S, P, r, hq, hkv, d, "full", seed=12)
+    for dsc in descs:
+        dsc.q_seg_len = 0
+    K, V = dev_chunks(ks, hkv, d), dev_chunks(vs, hkv, d)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    dummy_q = torch.zeros((1, hq, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((1, hq, d), 5.0, **f32)
+    lse = torch.full((hq, 1), 5.0, **f32)
+    B().ring_attn_fwd_chunks(descs, dummy_q, K, V, o, lse)
+    dq = torch.full((1, hq, d), 5.0, **f32)
+    dk = [torch.full((len(a), hkv, d), float("nan"), **f32) for a in ks]
+    dv = [torch.full((len(a), hkv, d), float("nan"), **f32) for a in ks]
+    B().ring_attn_bwd_chunks(descs, dummy_q, K, V, dummy_q, lse, lse, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert bool((o == 5.0).all()) and bool((lse == 5.0).all()) and bool((dq == 5.0).all())
+    assert all(bool((t == 0).all()) for t in dk + dv)
