@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_F32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector (published)
 
 
 def log(msg):
@@ -342,6 +343,7 @@ def main():
     n_launch = len(ring.launches)   # P, or 2P with the block A / block B rings
     # with --merge chunks the backward is one call over all steps
     chunks = args.merge == "chunks"
+    roof_peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_VECTOR_TFLOPS
     bwd_launch_flops = bwd_flops if chunks else bwd_flops / n_launch
     # with --merge chunks the forward is one launch over all steps
     fwd_launch_flops = fwd_flops if chunks else fwd_flops / n_launch
@@ -382,12 +384,15 @@ def main():
         "lse_merge_gbs": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms else None,
         "bwd_delta_gbs": round(delta_bytes / (delta_ms * 1e-3) / 1e9, 1) if delta_ms else None,
         # with --merge chunks the dominant call is ring_attn_bwd_chunks (its dQ
-        # launch and one dK/dV launch per chunk); the recorded counters are the
-        # per-step kernels', so they are not quoted for it
-        "roofline": {"bound": "mfma", "kernel": "ring_attn_bwd_chunks" if chunks else "ring_attn_step_bwd",
+        # launch and its dK/dV launch over all chunks); the recorded counters are
+        # the per-step kernels', so they are not quoted for it. The fp32
+        # workload runs plain fp32 vector kernels: bounded by the fp32 vector
+        # peak, not the matrix cores.
+        "roofline": {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+                     "kernel": "ring_attn_bwd_chunks" if chunks else "ring_attn_step_bwd",
                      "achieved": round(bwd_tflops, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "peak": roof_peak, "unit": "TFLOP/s",
+                     "frac": round(bwd_tflops / roof_peak, 4),
                      "traffic": None if chunks else recorded_traffic(cfg.name)},
     }
     util = None if chunks else recorded_mfma_util(cfg.name)
