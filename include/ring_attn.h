@@ -206,7 +206,7 @@ ra_status ring_attn_step_bwd(const ra_step_desc* desc, const void* q, const void
  * updated (in place), e.g. the rows a ring step gave any visible key: with
  * paired blocks, a chunk later than the rank's own is seen by block B only.
  * RA_EINVAL unless 0 <= row_begin <= rows and 0 <= row_count <= rows - row_begin;
- * row_count == 0 is a no-op.
+ * RA_EUNSUPPORTED for rows * hq >= 2^32; row_count == 0 is a no-op.
  */
 ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, int64_t row_begin,
                     int64_t row_count, float* o_acc, float* lse_acc, const float* o_step,
@@ -219,7 +219,7 @@ ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, int64_t row_begi
  *   delta[h][i] = sum_x dout[i][h][x] * o[i][h][x]
  * and, if o_out != NULL, o_out = o rounded to bf16 (nearest even).
  * o: fp32 [rows][hq][d]; dout: dtype [rows][hq][d]; o_out: bf16 [rows][hq][d];
- * all contiguous. delta: fp32 [hq][rows].
+ * all contiguous. delta: fp32 [hq][rows]. RA_EUNSUPPORTED for rows * hq >= 2^32.
  */
 ra_status ra_bwd_delta(int64_t rows, int32_t hq, int32_t head_dim, int32_t dtype,
                        const float* o, const void* dout, float* delta, void* o_out,

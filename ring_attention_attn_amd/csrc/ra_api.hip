@@ -266,6 +266,7 @@ ra_status lse_merge(int64_t rows, int32_t hq, int32_t head_dim, int64_t row_begi
   if (row_begin < 0 || row_count < 0 || row_begin > rows || row_count > rows - row_begin)
     return RA_EINVAL;
   if (head_dim != 64 && head_dim != 128) return RA_EUNSUPPORTED;
+  if (rows * (int64_t)hq > (int64_t)UINT32_MAX) return RA_EUNSUPPORTED;  // 32-bit row index
   if (row_count == 0) return RA_OK;
   if (!o_acc || !lse_acc || !o_step || !lse_step) return RA_EINVAL;
   if (!aligned16(o_acc) || !aligned16(o_step) || !aligned16(lse_acc) || !aligned16(lse_step))
@@ -279,6 +280,7 @@ ra_status ra_bwd_delta(int64_t rows, int32_t hq, int32_t head_dim, int32_t dtype
   if (rows < 0 || hq < 1) return RA_EINVAL;
   if (dtype != RA_BF16 && dtype != RA_F32) return RA_EINVAL;
   if (head_dim != 64 && head_dim != 128) return RA_EUNSUPPORTED;
+  if (rows * (int64_t)hq > (int64_t)UINT32_MAX) return RA_EUNSUPPORTED;  // 32-bit row index
   if (rows == 0) return RA_OK;
   if (!o || !dout || !delta) return RA_EINVAL;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta) || (o_out && !aligned16(o_out)))

@@ -37,8 +37,10 @@ __global__ __launch_bounds__(kBlock) void lse_merge_kernel(int64_t rows, int32_t
        t += (int64_t)gridDim.x * kBlock) {
     const int64_t vec = row_begin * hq + t / TPV;  // (row, head) pair, row-major
     const int x4 = (int)(t % TPV);
-    const int64_t row = vec / hq;
-    const int h = (int)(vec % hq);
+    // (rows * hq < 2^32, checked by the caller: 32-bit division)
+    const uint32_t v32 = (uint32_t)vec;
+    const int64_t row = (int64_t)(v32 / (uint32_t)hq);
+    const int h = (int)(v32 % (uint32_t)hq);
     const int64_t li = (int64_t)h * rows + row;
     const float la = lse_acc[li];
     const float ls = lse_step[li];
@@ -48,11 +50,13 @@ __global__ __launch_bounds__(kBlock) void lse_merge_kernel(int64_t rows, int32_t
     const float tot = ea + es;
     const float inv = 1.0f / tot;
     const float ca = ea * inv, cs = es * inv;
+    // O is streamed once: non-temporal 16-byte loads and stores
     f32x4* oa = reinterpret_cast<f32x4*>(o_acc + vec * D) + x4;
-    const f32x4 os = reinterpret_cast<const f32x4*>(o_step + vec * D)[x4];
-    f32x4 a = *oa;
+    const f32x4 os =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o_step + vec * D) + x4);
+    f32x4 a = __builtin_nontemporal_load(oa);
     a = ca * a + cs * os;
-    *oa = a;
+    __builtin_nontemporal_store(a, oa);
     if (x4 == 0) lse_acc[li] = m + logf(tot);
   }
 }
@@ -76,16 +80,18 @@ __global__ __launch_bounds__(kBlock) void bwd_delta_kernel(int64_t rows, int32_t
     const int sub = (int)(t % G);
     float acc = 0.f;
     if (valid) {
+      // O and dO are streamed once: non-temporal 16-byte loads (and stores)
       const f32x4* op = reinterpret_cast<const f32x4*>(o + vec * D + sub * 8);
-      const f32x4 o0 = op[0], o1 = op[1];
+      const f32x4 o0 = __builtin_nontemporal_load(op), o1 = __builtin_nontemporal_load(op + 1);
       float dv[8];
       if (BF16) {
-        const bf16x8 g8 = *reinterpret_cast<const bf16x8*>((const bf16_t*)dout + vec * D + sub * 8);
+        const bf16x8 g8 = __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x8*>((const bf16_t*)dout + vec * D + sub * 8));
 #pragma unroll
         for (int e = 0; e < 8; ++e) dv[e] = (float)g8[e];
       } else {
         const f32x4* gp = reinterpret_cast<const f32x4*>((const float*)dout + vec * D + sub * 8);
-        const f32x4 g0 = gp[0], g1 = gp[1];
+        const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { dv[e] = g0[e]; dv[4 + e] = g1[e]; }
       }
@@ -95,14 +101,16 @@ __global__ __launch_bounds__(kBlock) void bwd_delta_kernel(int64_t rows, int32_t
         bf16x8 ob;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { ob[e] = (bf16_t)o0[e]; ob[4 + e] = (bf16_t)o1[e]; }
-        *reinterpret_cast<bf16x8*>(o_out + vec * D + sub * 8) = ob;
+        __builtin_nontemporal_store(ob, reinterpret_cast<bf16x8*>(o_out + vec * D + sub * 8));
       }
     }
 #pragma unroll
     for (int off = G / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, G);
     if (valid && sub == 0) {
-      const int64_t row = vec / hq;
-      const int h = (int)(vec % hq);
+      // (rows * hq < 2^32, checked by the caller: 32-bit division)
+      const uint32_t v32 = (uint32_t)vec;
+      const int64_t row = (int64_t)(v32 / (uint32_t)hq);
+      const int h = (int)(v32 % (uint32_t)hq);
       delta[(int64_t)h * rows + row] = acc;
     }
   }

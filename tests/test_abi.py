@@ -145,11 +145,14 @@ def test_calls_reject_before_device_work():
     for call, code in [
         (lambda: B.lse_merge(-1, 4, 128, 16, 16, 16, 16, stream=0), B.RA_EINVAL),
         (lambda: B.lse_merge(8, 4, 80, 16, 16, 16, 16, stream=0), B.RA_EUNSUPPORTED),
+        (lambda: B.lse_merge(1 << 28, 32, 128, 16, 16, 16, 16, stream=0), B.RA_EUNSUPPORTED),
         (lambda: B.lse_merge(8, 4, 128, 16, 16, 16, 8, stream=0), B.RA_EALIGN),
         (lambda: B.lse_merge(8, 4, 128, 16, 16, 16, 16, stream=0, row_begin=-1), B.RA_EINVAL),
         (lambda: B.lse_merge(8, 4, 128, 16, 16, 16, 16, stream=0, row_begin=4, row_count=5),
          B.RA_EINVAL),                                                   # past the last row
         (lambda: B.ra_bwd_delta(8, 4, 128, 5, 16, 16, 16, stream=0), B.RA_EINVAL),
+        (lambda: B.ra_bwd_delta(1 << 28, 32, 128, B.RA_BF16, 16, 16, 16, stream=0),
+         B.RA_EUNSUPPORTED),
         (lambda: B.head_permute(16, 4096, 8, 6, 128, 4, 2, stream=0), B.RA_EINVAL),   # H % P
         (lambda: B.head_permute(16, 4096, 8, 8, 4, 8, 2, stream=0), B.RA_EALIGN),     # 8-byte runs
         (lambda: B.head_permute(16, 32, 8, 8, 128, 4, 2, stream=0), B.RA_EINVAL),     # overlap
