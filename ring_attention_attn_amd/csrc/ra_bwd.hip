@@ -438,7 +438,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_chunks_kernel(StepParams p, int
 //      the d columns 64 hf / (D/128) .. of its half, its own rows' P/dS from
 //      registers and its partner's from LDS. Q and dO tiles reach LDS by DMA
 //      one step ahead (two buffers each, XOR-swizzled), with the tile's LSE
-//      (log2 units) and D. Every dK/dV element has one writer.
+//      (log2 units) and -D. Every dK/dV element has one writer.
 //      The workgroup's KV head g and key block kt come from its caller.
 template <int D>
 __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, const int kt) {
@@ -449,13 +449,22 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
   constexpr int NDH = D / 64;  // 32-wide d blocks in a wave's half of d
   constexpr int TB = QT * D;   // elements per Q / dO tile
   constexpr int XB = 4 * 64 * 8;  // exchange elements per wave: 4 chunks x 64 lanes x 8
-  __shared__ __attribute__((aligned(1024))) bf16_t sQ0[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sQ1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sG0[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sG1[TB];
-  __shared__ __attribute__((aligned(1024))) bf16_t sX[NW * XB];  // P and dS hand-off
-  __shared__ __attribute__((aligned(16))) float sL[2][QT];  // LSE * log2(e) (+inf: no contribution)
-  __shared__ __attribute__((aligned(16))) float sD[2][QT];
+  // one LDS block at fixed byte offsets: the Q and dO tiles of buffers 0 and 1
+  // in the low 64 KiB (so every read of a tile reaches its buffer through the
+  // instruction's immediate offset, with no per-step address arithmetic), then
+  // the P / dS hand-off, LSE * log2(e) (+inf: no contribution) and -D
+  constexpr int TBB = TB * 2, XBB = NW * XB * 2;
+  constexpr int oQ0 = 0, oG0 = TBB, oQ1 = 2 * TBB, oG1 = 3 * TBB, oX = 4 * TBB;
+  constexpr int oL = oX + XBB, oD = oL + 2 * QT * 4, kLdsBytes = oD + 2 * QT * 4;
+  static_assert(4 * TBB <= 65536, "tile buffers must lie within the immediate offset's reach");
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  bf16_t* const sQ0 = (bf16_t*)(lds + oQ0);
+  bf16_t* const sQ1 = (bf16_t*)(lds + oQ1);
+  bf16_t* const sG0 = (bf16_t*)(lds + oG0);
+  bf16_t* const sG1 = (bf16_t*)(lds + oG1);
+  bf16_t* const sX = (bf16_t*)(lds + oX);
+  float(*const sL)[QT] = (float(*)[QT])(lds + oL);
+  float(*const sD)[QT] = (float(*)[QT])(lds + oD);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -536,7 +545,7 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
     constexpr int B = decltype(b)::value;
     if (wave == 0) {
       sL[B][lane] = pl == -INFINITY ? INFINITY : pl * kLog2e;  // empty row: no contribution
-      sD[B][lane] = pd;
+      sD[B][lane] = -pd;
     }
   };
 
@@ -548,6 +557,18 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
   const int roff = 32 * hf * 2 * D + swz_off<D>(srow, hi);
   const int toff0 = swz_off<D>(8 * hi + (gi >> 2), 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
   const int toff1 = swz_off<D>(8 * hi + (gi >> 2) + 4, 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  // the transposing reads' offsets for rows 32 hf' .. of the tile (hf' = hf:
+  // this wave's rows, hf ^ 1: its partner's) and the wave's d block db (XOR 64
+  // of the 32-wide block's index)
+  int tro[2][NDH][2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      const int rowb = 32 * (hf ^ w) * 2 * D, dblk = 64 * (NDH * hf + db);
+      tro[w][db][0] = rowb + (toff0 ^ dblk);
+      tro[w][db][1] = rowb + (toff1 ^ dblk);
+    }
   // hand-off slots: chunk cq (16 rows) of wave w at sX[w][cq][lane][8]
   bf16_t* const x_mine = sX + wave * XB + lane * 8;
   const bf16_t* const x_partner = sX + (wave ^ 4) * XB + lane * 8;
@@ -561,22 +582,27 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
     const char* cQ = (const char*)(B ? sQ1 : sQ0);
     const char* cG = (const char*)(B ? sG1 : sG0);
     sacc = f32x16{};
-    pacc = f32x16{};
+    // dP accumulates onto -D of its rows (read first, ahead of the operands),
+    // so the products leave dP - D: register r is row 32 hf + 16 (r/8) + 8 hi + r%8
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 nd = *(const f32x4*)(&sD[B][32 * hf + 16 * (j >> 1) + 8 * hi + 4 * (j & 1)]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pacc[4 * j + e] = nd[e];
+    }
     // the Q and dO row operands are read AH steps before their use, in a
     // fixed issue order (each fence keeps the compiler from moving
     // instructions across it), so the LDS latency hides behind the products
     constexpr int AH = 3;
     bf16x8 qa[AH + 1], ga[AH + 1];
-    // LSE and D of row chunk cc: chunk 0's are read among the last products
-    // (after the last operand read), chunk 1's at the start of chunk 0's
-    // vector work, so neither waits on the LDS before its first use
-    f32x4 ld[2][4];
+    // LSE of row chunk cc: chunk 0's are read among the last products (after
+    // the last operand read), chunk 1's at the start of chunk 0's vector work,
+    // so neither waits on the LDS before its first use
+    f32x4 ld[2][2];
     auto read_ld = [&](int cc) {
       const int qo = 32 * hf + 16 * cc + 8 * hi;
       ld[cc][0] = *(const f32x4*)(&sL[B][qo]);
       ld[cc][1] = *(const f32x4*)(&sL[B][qo + 4]);
-      ld[cc][2] = *(const f32x4*)(&sD[B][qo]);
-      ld[cc][3] = *(const f32x4*)(&sD[B][qo + 4]);
     };
 #pragma unroll
     for (int i = 0; i < AH; ++i) {
@@ -612,9 +638,8 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float l2 = e < 4 ? ld[cc][0][e] : ld[cc][1][e - 4];
-        const float dl = e < 4 ? ld[cc][2][e] : ld[cc][3][e - 4];
         pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * cc + e], p.scale_log2, -l2));
-        sv[e] = pv[e] * (pacc[8 * cc + e] - dl);
+        sv[e] = pv[e] * pacc[8 * cc + e];  // P (dP - D)
       }
       pk[cc] = pack_bf16x8(pv);
       dsk[cc] = pack_bf16x8(sv);
@@ -631,19 +656,15 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
   // latency hides behind the products in flight.
   auto phase2 = [&](auto b) {
     constexpr int B = decltype(b)::value;
-    // rows 32 hf' .. of the tile, hf' = the half of the chunk's owner
     const char* cQ = (const char*)(B ? sQ1 : sQ0);
     const char* cG = (const char*)(B ? sG1 : sG0);
-    const int own_row = 32 * hf * 2 * D, partner_row = 32 * (hf ^ 1) * 2 * D;
     constexpr int NM = 8 * NDH;
     constexpr int AHEAD = 3;
     auto a_op = [&](int m) -> bf16x8 {
       const int k = m / (2 * NDH), db = (m / 2) % NDH;
-      const int rowb = (k < 2 ? own_row : partner_row) + 16 * (k & 1) * 2 * D;
-      const int dblk = 64 * (NDH * hf + db);  // byte XOR of the 32-wide d block
-      const char* a = ((m & 1) ? cQ : cG) + rowb;
-      return __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + (toff0 ^ dblk))),
-                                     ds_read_tr((const bf16_t*)(a + (toff1 ^ dblk))), 0, 1, 2,
+      const char* a = ((m & 1) ? cQ : cG) + 16 * (k & 1) * 2 * D;
+      return __builtin_shufflevector(ds_read_tr((const bf16_t*)(a + tro[k >> 1][db][0])),
+                                     ds_read_tr((const bf16_t*)(a + tro[k >> 1][db][1])), 0, 1, 2,
                                      3, 4, 5, 6, 7);
     };
     bf16x8 ar[AHEAD + 1];
