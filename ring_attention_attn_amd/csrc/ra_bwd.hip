@@ -516,14 +516,20 @@ __device__ __forceinline__ void bwd_dkv_body(const StepParams& p, const int g, c
     hh = t >= 0 ? 0 : p.group;
   };
 
-  DmaSwz<QT, D, NW, 3> qst, gst;
-  qst.init(p.q_ss, wave, lane);
-  gst.init(p.do_ss, wave, lane);
+  // waves 0-3 stage the Q tile, waves 4-7 the dO tile: each wave builds one
+  // buffer descriptor per step (the address arithmetic is scalar, and all
+  // eight waves issue it right after the step's barrier)
+  const bool stages_q = wave < NW / 2;
+  DmaSwz<QT, D, NW / 2, 3> dst;
+  dst.init(stages_q ? p.q_ss : p.do_ss, wave & (NW / 2 - 1), lane);
+  const bf16_t* const st_base = stages_q
+                                    ? (const bf16_t*)p.q + (int64_t)g * p.group * p.q_hs
+                                    : (const bf16_t*)p.dout + (int64_t)g * p.group * p.do_hs;
+  const int64_t st_hs = stages_q ? p.q_hs : p.do_hs;
   auto stage = [&](int hh, int t, auto b) {
     constexpr int B = decltype(b)::value;
-    const int h = g * p.group + hh;
-    qst.issue((const bf16_t*)p.q + (int64_t)h * p.q_hs, t * QT, (int)lq, B ? sQ1 : sQ0);
-    gst.issue((const bf16_t*)p.dout + (int64_t)h * p.do_hs, t * QT, (int)lq, B ? sG1 : sG0);
+    bf16_t* const to = stages_q ? (B ? sQ1 : sQ0) : (B ? sG1 : sG0);
+    dst.issue(st_base + hh * st_hs, t * QT, (int)lq, to);
   };
   // LSE and D of a tile: wave 0 loads them into registers one step before
   // they are written to LDS (at the start of the step before their tile's), so
